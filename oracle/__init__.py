@@ -1,0 +1,35 @@
+"""CPU oracle for the Beam MoE layer forward pass (test infrastructure only).
+
+This package is test infrastructure.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path (the HIP library
+and its Python binding) never does, and it shares no code with that path.
+
+Every function here is the plain definition of a step of the layer, written
+in NumPy with fp64 accumulation and rounding to fp32/bf16 at the points the
+layer fixes.  See oracle/moe.py for the step-by-step citations.
+
+Parity status of each function:
+  codecs.bf16_round_bits / bf16_to_f64 / e4m3_decode  -- pinned (library casts, all codes)
+  moe.router_scores / select_experts / route          -- pinned (brute force, invariants,
+                                                          the G=1 plain top-k special case)
+  moe.permute                                          -- pinned (stable argsort, invariants)
+  moe.expert_rows / forward                            -- pinned (naive loops, identical-
+                                                          experts special case, dense-MLP
+                                                          reduction)
+  moe.forward at the real shape                        -- values are the definition; the
+                                                          pages print no worked example
+"""
+from . import codecs, moe  # noqa: F401
+from .moe import (  # noqa: F401
+    LayerSpec,
+    router_logits,
+    router_scores,
+    select_experts,
+    combine_weights,
+    route,
+    gap_violations,
+    permute,
+    expert_rows,
+    combine,
+    forward,
+)

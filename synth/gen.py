@@ -1,0 +1,243 @@
+"""Seeded generators for the synthetic MoE-layer workloads.
+
+Shapes and value distributions follow the Beam MoE block as the pages state it
+(Reflection Beam 1.0 overview, agentlenshq.com, section "Mixture of Experts":
+hidden 5120, 256 SwiGLU experts of intermediate size 2560 in 8 groups of 32,
+top-4 groups, top-8 experts, weights scaled by 2.5).  No trained weights exist
+in this setting, so every tensor is drawn from a fixed distribution:
+
+    x        ~ N(0, 1)      -> bf16           [T, H]
+    W_router ~ N(0, s_r)    fp32              [H, E]   (s_r = 0.05 tiny, 0.02 real shape)
+    b_router                fp32              [E]      (zero, fitted-balanced, or N(0, 1.5))
+    W_gate, W_up ~ N(0, 0.02) -> bf16         [E, I, H] (out, in: the reduction dim is contiguous)
+    W_down       ~ N(0, 0.02) -> bf16         [E, H, I]
+    fp8 workloads: the same fp32 draw, quantised per output channel to OCP e4m3
+    with scale = max_in |w| / 448 (fp32).
+
+Every tensor comes from its own stream, numpy.random.default_rng(
+[seed, workload_id, tensor_id, index]); tensor ids: 0 x, 1 W_router, 2 bias,
+3 W_gate, 4 W_up, 5 W_down, 6 re-drawn x rows.  Expert matrices are drawn one
+expert at a time, so any single expert can be regenerated on the CPU without
+touching the rest.
+
+fp32 -> bf16 and fp32 -> e4m3 conversions use torch's CPU casts (round to
+nearest even); they are input preparation, not the layer's arithmetic.
+"""
+from __future__ import annotations
+
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+X_ID, WR_ID, B_ID, WG_ID, WU_ID, WD_ID, REDRAW_ID = 0, 1, 2, 3, 4, 5, 6
+E4M3_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int            # workload id used in the seed tuple
+    T: int              # tokens
+    hidden: int         # H
+    inter: int          # I
+    n_experts: int      # E
+    n_groups: int       # G
+    topk_groups: int    # Gk
+    top_k: int          # K
+    alpha: float        # routed scale
+    sigma_router: float
+    sigma_expert: float
+    bias: str           # "zero" | "balanced" | "skew"
+    weight: str         # "bf16" | "fp8"
+
+    def with_T(self, T: int) -> "Workload":
+        return replace(self, T=T)
+
+
+def _real(name, wid, T, bias="zero", weight="bf16"):
+    return Workload(name, wid, T, 5120, 2560, 256, 8, 4, 8, 2.5, 0.02, 0.02, bias, weight)
+
+
+WORKLOADS = {
+    # tiny layer, same routing structure: 32 experts in 8 groups of 4
+    "tiny": Workload("tiny", 1, 64, 256, 128, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "bf16"),
+    # real shape, decode regime: weight streaming
+    "decode": _real("decode", 2, 64),
+    # real shape, prefill regime with near-balanced expert loads
+    "prefill": _real("prefill", 3, 8192, bias="balanced"),
+    # real shape, skewed routing from a per-expert logit offset ~ N(0, 1.5)
+    "skew": _real("skew", 4, 4096, bias="skew"),
+    # real shape, e4m3 expert weights + per-output-channel fp32 scales
+    "fp8_decode": _real("fp8_decode", 5, 32, weight="fp8"),
+    "fp8_prefill": _real("fp8_prefill", 5, 2048, weight="fp8"),
+}
+
+
+def workload(name: str, T: Optional[int] = None) -> Workload:
+    w = WORKLOADS[name]
+    return w if T is None else w.with_T(T)
+
+
+# ---------------------------------------------------------------- casts ----
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 array -> bf16 bit patterns (uint16), round to nearest even (torch CPU cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP e4m3fn bytes, round to nearest even, saturating at +-448."""
+    t = torch.from_numpy(np.clip(a, -E4M3_MAX, E4M3_MAX).astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _rng(seed, wid, tid, idx=0):
+    return np.random.default_rng([seed, wid, tid, idx])
+
+
+# ------------------------------------------------------- router inputs ----
+
+def _draw_x_rows(w: Workload, seed: int, rows: np.ndarray, rnd: int) -> np.ndarray:
+    out = np.empty((len(rows), w.hidden), np.float32)
+    for i, r in enumerate(rows):
+        out[i] = _rng(seed, w.wid, REDRAW_ID, rnd * 1_000_003 + int(r)).standard_normal(
+            w.hidden, dtype=np.float32)
+    return bf16_bits(out)
+
+
+def balanced_bias_path(seed: int) -> str:
+    return os.path.join(_HERE, f"prefill_bias_seed{seed}.txt")
+
+
+def load_balanced_bias(seed: int, n_experts: int) -> np.ndarray:
+    """The fitted bias column of the balanced prefill workload.
+
+    The file holds fp32 bit patterns in hex, one per expert, written by
+    oracle/fit_prefill_bias.py (which fits it with the oracle's routing).
+    """
+    path = balanced_bias_path(seed)
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"no fitted balanced bias for seed {seed} ({path}); "
+            "run python -m oracle.fit_prefill_bias --seed N")
+    vals = [int(line.split()[0], 16) for line in open(path)
+            if line.strip() and not line.startswith("#")]
+    b = np.array(vals, np.uint32).view(np.float32)
+    if b.shape != (n_experts,):
+        raise ValueError(f"{path}: expected {n_experts} values, got {b.shape}")
+    return b
+
+
+def router_inputs(w: Workload, seed: int = 0, bias: Optional[np.ndarray] = None):
+    """Return (x_bits uint16 [T,H], W_router fp32 [H,E], b_router fp32 [E])."""
+    x = _rng(seed, w.wid, X_ID).standard_normal((w.T, w.hidden), dtype=np.float32)
+    x_bits = bf16_bits(x)
+    wr = _rng(seed, w.wid, WR_ID).standard_normal((w.hidden, w.n_experts), dtype=np.float32)
+    wr *= np.float32(w.sigma_router)
+    if bias is not None:
+        b = np.asarray(bias, np.float32)
+    elif w.bias == "zero":
+        b = np.zeros(w.n_experts, np.float32)
+    elif w.bias == "skew":
+        b = _rng(seed, w.wid, B_ID).standard_normal(w.n_experts, dtype=np.float32)
+        b *= np.float32(1.5)
+    elif w.bias == "balanced":
+        b = load_balanced_bias(seed, w.n_experts)
+    else:
+        raise ValueError(w.bias)
+    return x_bits, wr, b
+
+
+def redraw_rows(x_bits: np.ndarray, w: Workload, seed: int, rows, rnd: int) -> np.ndarray:
+    """Replace the given token rows with fresh N(0,1) draws from the re-draw stream."""
+    rows = np.asarray(rows, np.int64)
+    out = x_bits.copy()
+    if len(rows):
+        out[rows] = _draw_x_rows(w, seed, rows, rnd)
+    return out
+
+
+def guarded_router_inputs(w: Workload, seed: int,
+                          violations: Callable[[np.ndarray, np.ndarray, np.ndarray], np.ndarray],
+                          max_rounds: int = 16, bias: Optional[np.ndarray] = None):
+    """router_inputs() with rows re-drawn until `violations` returns none.
+
+    `violations(x_bits, W_router, b)` is supplied by the caller (the tests pass
+    the oracle's score-gap check); this module does not compute scores itself.
+    Returns (x_bits, W_router, b, n_redrawn).
+    """
+    x_bits, wr, b = router_inputs(w, seed, bias)
+    n = 0
+    for rnd in range(max_rounds):
+        bad = np.asarray(violations(x_bits, wr, b))
+        if len(bad) == 0:
+            return x_bits, wr, b, n
+        n += len(bad)
+        x_bits = redraw_rows(x_bits, w, seed, bad, rnd)
+    raise RuntimeError(f"gap guard still violated after {max_rounds} re-draw rounds")
+
+
+# ------------------------------------------------------ expert weights ----
+
+def expert_matrix(w: Workload, seed: int, which: str, e: int):
+    """One expert's matrix.
+
+    which: "gate" | "up" -> [I, H]; "down" -> [H, I].
+    bf16 workloads return uint16 bit patterns; fp8 workloads return
+    (uint8 e4m3 codes, fp32 scale [out]) with scale = max|w| / 448 per row.
+    """
+    tid = {"gate": WG_ID, "up": WU_ID, "down": WD_ID}[which]
+    shape = (w.inter, w.hidden) if which in ("gate", "up") else (w.hidden, w.inter)
+    a = _rng(seed, w.wid, tid, e).standard_normal(shape, dtype=np.float32)
+    a *= np.float32(w.sigma_expert)
+    if w.weight == "bf16":
+        return bf16_bits(a)
+    amax = np.abs(a).max(axis=1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = _e4m3_codes(a / safe[:, None])
+    return q, scale
+
+
+class ExpertSource:
+    """Lazily generated expert weights on the host, one expert at a time.
+
+    get(which, e) returns what expert_matrix() returns; results are cached.
+    prefetch(experts) generates a set of experts with a thread pool.
+    """
+
+    def __init__(self, w: Workload, seed: int = 0, threads: Optional[int] = None):
+        self.w, self.seed = w, seed
+        self.threads = threads or min(16, len(os.sched_getaffinity(0)))
+        self._cache = {}
+        self._lock = threading.Lock()
+
+    def get(self, which: str, e: int):
+        key = (which, int(e))
+        with self._lock:
+            if key in self._cache:
+                return self._cache[key]
+        v = expert_matrix(self.w, self.seed, which, int(e))
+        with self._lock:
+            self._cache[key] = v
+        return v
+
+    def prefetch(self, experts):
+        keys = [(wh, int(e)) for e in experts for wh in ("gate", "up", "down")]
+        with ThreadPoolExecutor(self.threads) as ex:
+            list(ex.map(lambda k: self.get(*k), keys))
+
+    def drop(self):
+        self._cache.clear()
