@@ -1,0 +1,206 @@
+"""Benchmark of the Beam MoE block forward pass on one MI355X.
+
+    python bench.py [--workload decode|prefill|skew|fp8_decode|fp8_prefill] [--steps K] [--warmup W]
+
+A step is one beam_moe_forward call (router, selection, permutation, gate/up
+GEMM + SwiGLU, down GEMM, combine) over one batch of seeded synthetic inputs
+already resident in HBM.  The timed region is bracketed by device
+synchronisation; per-kernel durations come from HIP events that the library
+records on its own stream between stages (beam_moe_forward_timed).
+
+Prints one JSON line: tokens/s (value), the whole layer's HBM GB/s and expert
+TFLOP/s with their fractions of MI355X's peaks, a roofline entry for the
+dominant kernel (gate/up), and the CPU oracle timed on a bounded sample of the
+same workload on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MFMA TFLOP/s (prefill) vs peak, 1 GPU"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+STAGES = ["router_logits", "router_select", "permute", "gateup", "down", "combine"]
+DEFAULTS = {"decode": (200, 20), "fp8_decode": (200, 20), "prefill": (30, 5), "skew": (40, 5), "fp8_prefill": (60, 5)}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("experts.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "sparse_moe_layer_top_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0):
+    """The oracle as it stands, on a bounded token sample of the same workload (host cores)."""
+    import oracle
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    spec = oracle.LayerSpec.of(w)
+    n = 2 if w.T >= 2 else 1
+    src = gen.ExpertSource(w, 0)
+    total_t, total_tok = 0.0, 0
+    start = 0
+    while start < w.T and (total_t < seconds_target or total_tok == 0):
+        sel = slice(start, min(start + n, w.T))
+        ids, _ = oracle.route(spec, x_bits[sel], wr, b)
+        src.prefetch(np.unique(ids))        # input generation: not timed
+        t0 = time.perf_counter()
+        oracle.forward(spec, x_bits[sel], wr, b, src.get)
+        total_t += time.perf_counter() - t0
+        total_tok += sel.stop - sel.start
+        src.drop()
+        start = sel.stop
+        if total_t > seconds_target * 0.5:
+            break
+    return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), full layer per token, "
+                      f"{total_t:.1f} s of oracle time, weight generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is not built here", file=sys.stderr)
+        sys.exit(2)
+    steps, warmup = DEFAULTS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+
+    import torch
+    import sparse_moe_layer_top_amd as bm
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    w = gen.workload(args.workload)
+    fp8 = w.weight == "fp8"
+    cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha,
+                    bm.W_FP8_E4M3 if fp8 else bm.W_BF16)
+    log(f"[bench] {w.name}: T={w.T} H={w.hidden} I={w.inter} E={w.n_experts} weights={w.weight}")
+    x_bits, wr, b = gen.router_inputs(w, args.seed)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wr_t = torch.from_numpy(wr).to(dev)
+    b_t = torch.from_numpy(b).to(dev)
+    t0 = time.time()
+    W = gen.device_expert_weights(w, args.seed, dev, log=log)
+    log(f"[bench] expert weights on device in {time.time() - t0:.1f} s")
+    out = torch.empty(w.T, w.hidden, dtype=torch.bfloat16, device=dev)
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=dev)
+    ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        bm.beam_moe_forward(cfg, x, wr_t, b_t, W["gate"], W["up"], W["down"], W.get("s_gate"), W.get("s_up"),
+                            W.get("s_down"), out=out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
+                            stage_events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for row in evs:              # record once so each event exists before the library records it
+        for e in row:
+            e.record()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    start.record()
+    for i in range(steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, name in enumerate(STAGES)}
+
+    # routing statistics and algorithmic work of this batch
+    ids_h = ids.cpu().numpy()
+    load = np.bincount(ids_h.ravel(), minlength=w.n_experts)
+    D = int((load > 0).sum())
+    TK = w.T * w.top_k
+    wb = 1 if fp8 else 2
+    H, I = w.hidden, w.inter
+    scale_b = 4 if fp8 else 0
+    gu_bytes = D * (2 * I * H * wb + 2 * I * scale_b) + w.T * H * 2 + TK * I * 2
+    dn_bytes = D * (H * I * wb + H * scale_b) + TK * I * 2 + TK * H * 2
+    layer_bytes = D * (3 * I * H * wb + (2 * I + H) * scale_b) + H * w.n_experts * 4 + w.n_experts * 4 + 2 * w.T * H * 2
+    layer_flops = 6.0 * TK * H * I
+    gu_flops = 4.0 * TK * H * I
+    s = ms / 1e3
+    hbm_gbps = layer_bytes / s / 1e9
+    tflops = layer_flops / s / 1e12
+    decode_like = TK / w.n_experts < 64
+    t_gu = stage_ms["gateup"] / 1e3
+    if decode_like:
+        ach = gu_bytes / t_gu / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4)}
+    else:
+        ach = gu_flops / t_gu / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    roof["kernel"] = "gateup_stream_kernel"
+    roof["algorithmic_bytes_per_launch"] = gu_bytes
+    roof["traffic"] = load_traffic(w.name, "gateup")
+
+    res = {
+        "metric": METRIC, "value": round(w.T / s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8-e4m3 weights, bf16 MFMA" if fp8 else "bf16",
+        "data": "synthetic (seeded, random-init weights of the real layer shape)",
+        "config": {"workload": f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
+                               f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}",
+                   "T": w.T, "weights": w.weight, "bias": w.bias},
+        "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
+        "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "layer_bytes": layer_bytes, "layer_flops": layer_flops,
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "routing": {"touched_experts": D, "max_load": int(load.max()), "mean_load": TK / w.n_experts,
+                    "zero_load_experts": int((load == 0).sum())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(w, x_bits, wr, b)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * beam_moe.h -- C ABI of the Beam MoE block forward pass on one MI355X (gfx950).
+ *
+ * The operation (Reflection Beam 1.0 overview page, agentlenshq.com, section
+ * "Mixture of Experts: 256 experts, 8 routed per token"; the same statement on
+ * the aixai.ru page, section "256 experts per layer", and the dothoosh.com
+ * page, section "Architecture and memory efficiency"):
+ *
+ *   s[t,e]   = sigmoid( x[t,:] . W_router[:,e] + b[e] )          all E experts, FP32
+ *   groups   = E/G contiguous experts; group score = sum of its top-2 s
+ *   kept     = the Gk best groups; chosen = the K best experts inside them
+ *   w[t,k]   = alpha * s[t,e_k] / sum_k' s[t,e_k']                normalised, x alpha (2.5)
+ *   y_e(x)   = W_down[e] ( SiLU(W_gate[e] x) * (W_up[e] x) )       SwiGLU expert, product in FP32
+ *   out[t,:] = sum_k w[t,k] * y_{e_k}(x[t,:])                      no shared expert
+ *
+ * The overview page's "Residual stream" section lists the router and the
+ * SwiGLU product among the places computed in FP32.  Linear outputs (h after
+ * the SwiGLU product, each expert's y, the combined out) are rounded to bf16.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [device] are HIP device pointers; all others are host.
+ *     The caller owns every buffer; the library allocates nothing and keeps no
+ *     state between calls.  Device pointers must be 16-byte aligned.
+ *   - Matrices are row-major.  Expert weights are stored [E, out, in]: the
+ *     reduction dimension is contiguous.  bf16 tensors are passed as raw
+ *     16-bit patterns, e4m3 tensors as raw bytes (OCP e4m3fn: bias 7, max 448,
+ *     S.1111.111 = NaN).
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     null stream) and returns without synchronising.  No call reads results
+ *     back to the host, so calls can be captured into a HIP graph.
+ *   - Arguments are checked before anything is enqueued: a call that returns
+ *     an error has enqueued nothing (BEAM_MOE_ERR_HIP excepted: it reports a
+ *     failed launch).  T == 0 returns BEAM_MOE_OK with no work.
+ *   - Inputs are read-only and must not overlap outputs or the workspace.
+ *     Concurrent calls on different streams need separate workspaces.
+ *   - NaN or Inf in inputs give unspecified results.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BEAM_MOE_OK = 0,
+  BEAM_MOE_ERR_INVALID = -1,      /* null pointer, bad size, bad config */
+  BEAM_MOE_ERR_UNSUPPORTED = -2,  /* a valid configuration this build does not handle */
+  BEAM_MOE_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  BEAM_MOE_ERR_HIP = -4           /* a HIP launch failed */
+} beam_moe_status;
+
+typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1 } beam_moe_wtype;
+
+typedef enum { BEAM_MOE_OP_ROUTE = 0, BEAM_MOE_OP_PERMUTE = 1, BEAM_MOE_OP_FORWARD = 2 } beam_moe_op;
+
+/* Layer configuration (host struct, read at call time).
+ * Beam's real shape: hidden 5120, inter 2560, 256 experts in 8 groups of 32,
+ * 4 kept groups, top-8, alpha 2.5 (overview page, "Mixture of Experts"). */
+typedef struct {
+  int32_t hidden;       /* H: multiple of 64 */
+  int32_t inter;        /* I: multiple of 64 */
+  int32_t n_experts;    /* E: 1..256 */
+  int32_t n_groups;     /* G: 1..64, E % G == 0 */
+  int32_t topk_groups;  /* Gk: 1..G */
+  int32_t top_k;        /* K: 1..8, K <= Gk * E / G */
+  float routed_scale;   /* alpha: finite */
+  int32_t weight_type;  /* beam_moe_wtype */
+} beam_moe_config;
+
+/* Largest T accepted by every entry point. */
+#define BEAM_MOE_MAX_TOKENS 262144
+
+/* Static, NUL-terminated description of a status code (host only). */
+const char* beam_moe_status_string(int status);
+
+/* Workspace bytes that `op` needs for T tokens (host only, pure).
+ * Writes *bytes and returns BEAM_MOE_OK, or an error for an invalid cfg/T/op.
+ * The forward workspace holds the router partial logits, the routing table
+ * (unless the caller supplies it), the permutation, the per-row SwiGLU
+ * activations h [T*K, I] bf16 and the per-row expert outputs y [T*K, H] bf16. */
+int beam_moe_workspace_bytes(const beam_moe_config* cfg, int32_t T, int32_t op, size_t* bytes);
+
+/* Router and group-limited selection.
+ *   x          [device] [T, H] bf16 (the MoE block's input, i.e. the pre-normed hidden state)
+ *   w_router   [device] [H, E] fp32 (row h holds the E expert weights of input channel h)
+ *   b_router   [device] [E] fp32, or NULL for no bias column
+ *   topk_ids   [device] [T, K] int32 out: the K chosen experts, ascending expert id
+ *   topk_w     [device] [T, K] fp32 out: alpha * s / sum(s) over the K chosen, same order
+ *   workspace  [device] beam_moe_workspace_bytes(ROUTE) bytes (may be NULL if that is 0)
+ * Ties at a selection boundary go to the lower group index / lower expert id. */
+int beam_moe_route(const beam_moe_config* cfg, int32_t T,
+                   const void* x, const float* w_router, const float* b_router,
+                   int32_t* topk_ids, float* topk_w,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Token -> expert permutation of the T*K (token, slot) pairs p = t*K + k.
+ * On one GPU the dispatch to experts and the merge back (breadlab.ai Beam
+ * inference post, section "Reading 23B active and 501B resident separately")
+ * become this grouping and its inverse.
+ *   topk_ids        [device] [T, K] int32 in: distinct ids in [0, E) per token
+ *                   (as beam_moe_route writes them); other values give
+ *                   unspecified output but no out-of-bounds access
+ *   expert_offsets  [device] [E+1] int32 out: rows of expert e are [off[e], off[e+1]); off[E] = T*K
+ *   sorted_pairs    [device] [T*K] int32 out: pair index of each row; pairs grouped by
+ *                   expert, ascending p (so ascending token) within an expert
+ *   pair_to_row     [device] [T*K] int32 out: inverse of sorted_pairs
+ *   workspace       [device] beam_moe_workspace_bytes(PERMUTE) bytes
+ * Deterministic: the result does not depend on scheduling. */
+int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_ids,
+                     int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole block: route, permute, grouped SwiGLU experts, weighted combine.
+ *   x, w_router, b_router   as in beam_moe_route
+ *   w_gate, w_up   [device] [E, I, H] bf16, or e4m3 bytes when weight_type is FP8
+ *   w_down         [device] [E, H, I] bf16 or e4m3
+ *   s_gate, s_up   [device] [E, I] fp32 per-output-channel scales (FP8 only, else NULL)
+ *   s_down         [device] [E, H] fp32 (FP8 only, else NULL)
+ *                  an FP8 weight's value is decode(q) * scale[e, out]
+ *   out            [device] [T, H] bf16 out
+ *   topk_ids_out, topk_w_out  [device] optional [T, K] copies of the routing (may be NULL)
+ *   workspace      [device] beam_moe_workspace_bytes(FORWARD) bytes
+ * Combine sums the K weighted expert rows in fp32 in ascending expert id. */
+int beam_moe_forward(const beam_moe_config* cfg, int32_t T,
+                     const void* x, const float* w_router, const float* b_router,
+                     const void* w_gate, const void* w_up, const void* w_down,
+                     const float* s_gate, const float* s_up, const float* s_down,
+                     void* out, int32_t* topk_ids_out, float* topk_w_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* beam_moe_forward with stage timestamps, for measuring each kernel on the
+ * stream it runs on.  stage_events is NULL (then this is beam_moe_forward) or
+ * an array of 7 hipEvent_t created by the caller; event i is recorded on
+ * `stream` before stage i and event 6 after the last:
+ *   0 router logits | 1 router selection | 2 permutation (3 kernels) |
+ *   3 gate/up GEMM + SwiGLU | 4 down GEMM | 5 combine | 6 end. */
+int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T,
+                           const void* x, const float* w_router, const float* b_router,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           const float* s_gate, const float* s_up, const float* s_down,
+                           void* out, int32_t* topk_ids_out, float* topk_w_out,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -1,0 +1,214 @@
+"""Thin ctypes binding of libbeam_moe.so (the C ABI in include/beam_moe.h).
+
+Argument marshalling only: dtype/shape/device checks on torch tensors, then the
+raw device pointers and torch's current HIP stream go to the library, which
+enqueues every step of the path in its own kernels.  There is no fallback: if
+the library is not built, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbeam_moe.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+W_BF16, W_FP8_E4M3 = 0, 1
+OP_ROUTE, OP_PERMUTE, OP_FORWARD = 0, 1, 2
+MAX_TOKENS = 262144
+
+
+class BeamMoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float), ("weight_type", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Config:
+    """Layer shape: hidden H, inter I, E experts in G groups, keep Gk groups, top-K, scale alpha."""
+    hidden: int = 5120
+    inter: int = 2560
+    n_experts: int = 256
+    n_groups: int = 8
+    topk_groups: int = 4
+    top_k: int = 8
+    routed_scale: float = 2.5
+    weight_type: int = W_BF16
+
+    def c(self) -> _Config:
+        return _Config(self.hidden, self.inter, self.n_experts, self.n_groups, self.topk_groups, self.top_k,
+                       self.routed_scale, self.weight_type)
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run python sparse_moe_layer_top_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(_Config)
+    lib.beam_moe_status_string.argtypes = [ctypes.c_int]
+    lib.beam_moe_status_string.restype = ctypes.c_char_p
+    lib.beam_moe_workspace_bytes.argtypes = [cfgp, I32, I32, ctypes.POINTER(SZ)]
+    lib.beam_moe_workspace_bytes.restype = ctypes.c_int
+    lib.beam_moe_route.argtypes = [cfgp, I32, P, P, P, P, P, P, SZ, P]
+    lib.beam_moe_route.restype = ctypes.c_int
+    lib.beam_moe_permute.argtypes = [cfgp, I32, P, P, P, P, P, SZ, P]
+    lib.beam_moe_permute.restype = ctypes.c_int
+    lib.beam_moe_forward.argtypes = [cfgp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.beam_moe_forward.restype = ctypes.c_int
+    lib.beam_moe_forward_timed.argtypes = [cfgp, I32] + [P] * 13 + [SZ, P, P]
+    lib.beam_moe_forward_timed.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+LIB_PATH = _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return LIB.beam_moe_status_string(status).decode()
+
+
+def _check(fn: str, st: int):
+    if st != OK:
+        raise BeamMoeError(fn, st)
+
+
+def beam_moe_workspace_bytes(cfg: Config, T: int, op: int = OP_FORWARD) -> int:
+    n = ctypes.c_size_t(0)
+    _check("beam_moe_workspace_bytes", LIB.beam_moe_workspace_bytes(ctypes.byref(cfg.c()), T, op, ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype, shape, device=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(cfg, T, op, workspace, device):
+    need = beam_moe_workspace_bytes(cfg, T, op)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.device != device or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 device tensor of at least {need} bytes")
+    return workspace
+
+
+def beam_moe_route(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor] = None,
+                   topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Router + group-limited top-k.  x [T,H] bf16, w_router [H,E] fp32, b_router [E] fp32 or None.
+    Returns (topk_ids [T,K] int32 ascending, topk_w [T,K] fp32)."""
+    T, dev = x.shape[0], x.device
+    _need(x, "x", torch.bfloat16, (T, cfg.hidden))
+    _need(w_router, "w_router", torch.float32, (cfg.hidden, cfg.n_experts), dev)
+    _need(b_router, "b_router", torch.float32, (cfg.n_experts,), dev, optional=True)
+    if topk_ids is None:
+        topk_ids = torch.empty(T, cfg.top_k, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, (T, cfg.top_k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, cfg.top_k), dev)
+    ws = _workspace(cfg, T, OP_ROUTE, workspace, dev)
+    _check("beam_moe_route", LIB.beam_moe_route(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(b_router),
+                                                _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(dev)))
+    return topk_ids, topk_w
+
+
+def beam_moe_permute(cfg: Config, topk_ids: torch.Tensor, expert_offsets=None, sorted_pairs=None,
+                     pair_to_row=None, workspace: Optional[torch.Tensor] = None):
+    """Token -> expert permutation.  Returns (expert_offsets [E+1], sorted_pairs [T*K], pair_to_row [T*K])."""
+    T, dev = topk_ids.shape[0], topk_ids.device
+    _need(topk_ids, "topk_ids", torch.int32, (T, cfg.top_k))
+    n = T * cfg.top_k
+    if expert_offsets is None:
+        expert_offsets = torch.empty(cfg.n_experts + 1, dtype=torch.int32, device=dev)
+    if sorted_pairs is None:
+        sorted_pairs = torch.empty(n, dtype=torch.int32, device=dev)
+    if pair_to_row is None:
+        pair_to_row = torch.empty(n, dtype=torch.int32, device=dev)
+    _need(expert_offsets, "expert_offsets", torch.int32, (cfg.n_experts + 1,), dev)
+    _need(sorted_pairs, "sorted_pairs", torch.int32, (n,), dev)
+    _need(pair_to_row, "pair_to_row", torch.int32, (n,), dev)
+    ws = _workspace(cfg, T, OP_PERMUTE, workspace, dev)
+    _check("beam_moe_permute", LIB.beam_moe_permute(ctypes.byref(cfg.c()), T, _ptr(topk_ids), _ptr(expert_offsets),
+                                                    _ptr(sorted_pairs), _ptr(pair_to_row), _ptr(ws), ws.numel(),
+                                                    _stream(dev)))
+    return expert_offsets, sorted_pairs, pair_to_row
+
+
+def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor],
+                     w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                     s_gate: Optional[torch.Tensor] = None, s_up: Optional[torch.Tensor] = None,
+                     s_down: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     topk_ids_out: Optional[torch.Tensor] = None, topk_w_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stage_events=None) -> torch.Tensor:
+    """The whole MoE block.  Expert weights [E,I,H] / [E,H,I]: bf16, or uint8 e4m3 codes with fp32 scales.
+
+    stage_events: None, or 7 recorded torch.cuda.Event(enable_timing=True)
+    that the library records before each stage and after the last
+    (beam_moe_forward_timed)."""
+    T, dev = x.shape[0], x.device
+    E, H, I = cfg.n_experts, cfg.hidden, cfg.inter
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(w_router, "w_router", torch.float32, (H, E), dev)
+    _need(b_router, "b_router", torch.float32, (E,), dev, optional=True)
+    wdt = torch.uint8 if cfg.weight_type == W_FP8_E4M3 else torch.bfloat16
+    _need(w_gate, "w_gate", wdt, (E, I, H), dev)
+    _need(w_up, "w_up", wdt, (E, I, H), dev)
+    _need(w_down, "w_down", wdt, (E, H, I), dev)
+    fp8 = cfg.weight_type == W_FP8_E4M3
+    _need(s_gate, "s_gate", torch.float32, (E, I), dev, optional=not fp8)
+    _need(s_up, "s_up", torch.float32, (E, I), dev, optional=not fp8)
+    _need(s_down, "s_down", torch.float32, (E, H), dev, optional=not fp8)
+    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
+        raise ValueError("scales are only for fp8 weights")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _need(topk_ids_out, "topk_ids_out", torch.int32, (T, cfg.top_k), dev, optional=True)
+    _need(topk_w_out, "topk_w_out", torch.float32, (T, cfg.top_k), dev, optional=True)
+    ws = _workspace(cfg, T, OP_FORWARD, workspace, dev)
+    args = [ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up),
+            _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(out), _ptr(topk_ids_out),
+            _ptr(topk_w_out), _ptr(ws), ws.numel(), _stream(dev)]
+    if stage_events is None:
+        _check("beam_moe_forward", LIB.beam_moe_forward(*args))
+    else:
+        if len(stage_events) != 7 or any(ev.cuda_event == 0 for ev in stage_events):
+            raise ValueError("stage_events must be 7 torch.cuda.Event objects, each recorded once beforehand")
+        arr = (ctypes.c_void_p * 7)(*[ev.cuda_event for ev in stage_events])
+        _check("beam_moe_forward_timed", LIB.beam_moe_forward_timed(*args, arr))
+    return out

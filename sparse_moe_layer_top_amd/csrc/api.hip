@@ -1,0 +1,232 @@
+// C ABI of the Beam MoE block (declared in include/beam_moe.h): argument checks,
+// workspace carve-up and launch sequencing.  Allocates nothing, never
+// synchronises, keeps no state between calls.
+#include "beam_moe.h"
+
+#include <math.h>
+
+#include "common.h"
+
+using beam::Layout;
+using beam::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_config(const beam_moe_config* c) {
+  if (!c) return BEAM_MOE_ERR_INVALID;
+  if (c->hidden <= 0 || c->inter <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 ||
+      c->top_k <= 0)
+    return BEAM_MOE_ERR_INVALID;
+  if (c->n_experts % c->n_groups != 0) return BEAM_MOE_ERR_INVALID;
+  if (c->topk_groups > c->n_groups) return BEAM_MOE_ERR_INVALID;
+  if ((long)c->top_k > (long)c->topk_groups * (c->n_experts / c->n_groups)) return BEAM_MOE_ERR_INVALID;
+  if (!isfinite(c->routed_scale)) return BEAM_MOE_ERR_INVALID;
+  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3) return BEAM_MOE_ERR_INVALID;
+  if (c->hidden % 64 != 0 || c->inter % 64 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->n_experts > beam::kMaxExperts || c->n_groups > 64 || c->top_k > beam::kMaxTopK)
+    return BEAM_MOE_ERR_UNSUPPORTED;
+  return BEAM_MOE_OK;
+}
+
+Shape shape_of(const beam_moe_config* c) {
+  return Shape{c->hidden, c->inter, c->n_experts, c->n_groups, c->topk_groups, c->top_k, c->routed_scale,
+               c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
+}
+
+// Router K-split: kc = H/ks is a multiple of 32, between 128 and 1280 where
+// possible (short fp32 chains), and the grid should reach ~1024 workgroups.
+int choose_ks(const Shape& s, int T) {
+  const int units = s.H / 32;
+  const long blocks0 = (long)((T + 63) / 64) * ((s.E + 63) / 64);
+  int best = 1;
+  for (int ks = 1; ks <= units; ++ks) {
+    if (units % ks) continue;
+    const int kc = s.H / ks;
+    if (kc > 1280) continue;
+    if (kc < 128 && best != 1) break;
+    best = ks;
+    if (blocks0 * ks >= 1024) break;
+    if (kc <= 128) break;
+  }
+  return best;
+}
+
+Layout make_layout(const Shape& s, int T, int op) {
+  Layout L{};
+  const size_t TK = (size_t)T * s.K;
+  L.ks = choose_ks(s, T);
+  L.nchunks = (T + beam::kChunk - 1) / beam::kChunk;
+  const int bm = beam::expert_tile_rows(s, T);
+  L.max_tiles = (int)(TK / bm) + s.E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  if (op == BEAM_MOE_OP_ROUTE || op == BEAM_MOE_OP_FORWARD) L.logits = take((size_t)L.ks * T * s.E * 4);
+  if (op == BEAM_MOE_OP_PERMUTE || op == BEAM_MOE_OP_FORWARD) {
+    L.masks = take((size_t)L.nchunks * s.E * 8);
+    L.counts = take((size_t)L.nchunks * s.E * 4);
+  }
+  if (op == BEAM_MOE_OP_FORWARD) {
+    L.ids = take(TK * 4);
+    L.w = take(TK * 4);
+    L.offsets = take((size_t)(s.E + 1) * 4);
+    L.tiles = take((size_t)L.max_tiles * 8);
+    L.ntiles = take(4);
+    L.sorted = take(TK * 4);
+    L.p2r = take(TK * 4);
+    L.h = take(TK * s.I * 2);
+    L.y = take(TK * s.H * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+#define BEAM_TRY_HIP(expr)                               \
+  do {                                                   \
+    if ((expr) != hipSuccess) return BEAM_MOE_ERR_HIP;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_moe_status_string(int status) {
+  switch (status) {
+    case BEAM_MOE_OK: return "ok";
+    case BEAM_MOE_ERR_INVALID: return "invalid argument";
+    case BEAM_MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BEAM_MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case BEAM_MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int beam_moe_workspace_bytes(const beam_moe_config* cfg, int32_t T, int32_t op, size_t* bytes) {
+  const int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (!bytes || T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (op != BEAM_MOE_OP_ROUTE && op != BEAM_MOE_OP_PERMUTE && op != BEAM_MOE_OP_FORWARD) return BEAM_MOE_ERR_INVALID;
+  *bytes = T == 0 ? 0 : make_layout(shape_of(cfg), T, op).total;
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
+                   const float* b_router, int32_t* topk_ids, float* topk_w, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (T == 0) return BEAM_MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w) return BEAM_MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w) ||
+      (b_router && !aligned4(b_router)))
+    return BEAM_MOE_ERR_INVALID;
+  const Shape s = shape_of(cfg);
+  const Layout L = make_layout(s, T, BEAM_MOE_OP_ROUTE);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* partial = at<float>(workspace, L.logits);
+  BEAM_TRY_HIP(beam::launch_router_logits(s, T, L.ks, static_cast<const uint16_t*>(x), w_router, partial, hs));
+  BEAM_TRY_HIP(beam::launch_router_select(s, T, L.ks, partial, b_router, topk_ids, topk_w, hs));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_ids, int32_t* expert_offsets,
+                     int32_t* sorted_pairs, int32_t* pair_to_row, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (T == 0) return BEAM_MOE_OK;
+  if (!topk_ids || !expert_offsets || !sorted_pairs || !pair_to_row) return BEAM_MOE_ERR_INVALID;
+  if (!aligned4(topk_ids) || !aligned4(expert_offsets) || !aligned4(sorted_pairs) || !aligned4(pair_to_row))
+    return BEAM_MOE_ERR_INVALID;
+  const Shape s = shape_of(cfg);
+  const Layout L = make_layout(s, T, BEAM_MOE_OP_PERMUTE);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
+  BEAM_TRY_HIP(beam::launch_permute(s, T, topk_ids, L.nchunks, at<uint64_t>(workspace, L.masks),
+                                    at<int32_t>(workspace, L.counts), expert_offsets, sorted_pairs, pair_to_row,
+                                    0, nullptr, nullptr, static_cast<hipStream_t>(stream)));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
+                     const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+                     const float* s_gate, const float* s_up, const float* s_down, void* out, int32_t* topk_ids_out,
+                     float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return beam_moe_forward_timed(cfg, T, x, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, out,
+                                topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
+                           const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+                           const float* s_gate, const float* s_up, const float* s_down, void* out,
+                           int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* stage_events) {
+  int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (T == 0) return BEAM_MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
+  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
+  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
+    return BEAM_MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out) || (b_router && !aligned4(b_router)) || (topk_ids_out && !aligned4(topk_ids_out)) ||
+      (topk_w_out && !aligned4(topk_w_out)) || (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+    return BEAM_MOE_ERR_INVALID;
+  const Shape s = shape_of(cfg);
+  const Layout L = make_layout(s, T, BEAM_MOE_OP_FORWARD);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
+  float* partial = at<float>(workspace, L.logits);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* p2r = at<int32_t>(workspace, L.p2r);
+  int32_t* tiles = at<int32_t>(workspace, L.tiles);
+  int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
+  uint16_t* h = at<uint16_t>(workspace, L.h);
+  uint16_t* y = at<uint16_t>(workspace, L.y);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) : hipSuccess;
+  };
+
+  BEAM_TRY_HIP(mark(0));
+  BEAM_TRY_HIP(beam::launch_router_logits(s, T, L.ks, xb, w_router, partial, hs));
+  BEAM_TRY_HIP(mark(1));
+  BEAM_TRY_HIP(beam::launch_router_select(s, T, L.ks, partial, b_router, ids, w, hs));
+  BEAM_TRY_HIP(mark(2));
+  BEAM_TRY_HIP(beam::launch_permute(s, T, ids, L.nchunks, at<uint64_t>(workspace, L.masks),
+                                    at<int32_t>(workspace, L.counts), offsets, sorted, p2r,
+                                    beam::expert_tile_rows(s, T), tiles, ntiles, hs));
+  BEAM_TRY_HIP(mark(3));
+  BEAM_TRY_HIP(beam::launch_gateup(s, T, xb, w_gate, w_up, s_gate, s_up, offsets, sorted, tiles, ntiles,
+                                   L.max_tiles, h, hs));
+  BEAM_TRY_HIP(mark(4));
+  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, y, hs));
+  BEAM_TRY_HIP(mark(5));
+  BEAM_TRY_HIP(beam::launch_combine(s, T, y, w, p2r, static_cast<uint16_t*>(out), hs));
+  BEAM_TRY_HIP(mark(6));
+  return BEAM_MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Token -> expert permutation: per-chunk histogram, one-workgroup scan, stable scatter.
+//
+// On one GPU, sending each token to its experts and merging the results back
+// (breadlab.ai Beam inference post, section "Reading 23B active and 501B
+// resident separately") is a grouping of the T*K (token, slot) pairs by expert.
+// Pairs of an expert keep ascending pair order, with no value atomics, so the
+// result is the same on every run:
+//   hist:    one wave per chunk of 64 tokens builds, for every expert, a 64-bit
+//            mask of the chunk's tokens routed to it (LDS atomic OR: the result
+//            does not depend on the order), stores it and its popcount;
+//   scan:    one workgroup turns the per-chunk counts into per-chunk bases and
+//            the expert offsets, and (for the forward) lists the row tiles of
+//            the grouped GEMMs;
+//   scatter: a token's rank inside its chunk is the popcount of the mask bits
+//            below it, so row = offset[e] + base[chunk][e] + rank.
+// A token routes to each expert at most once, so one bit per token suffices.
+#include "common.h"
+
+namespace beam {
+
+__global__ __launch_bounds__(64) void perm_hist_kernel(int T, int E, int K, const int32_t* __restrict__ ids,
+                                                       uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
+  __shared__ uint64_t m[kMaxExperts];
+  const int c = blockIdx.x, lane = threadIdx.x;
+  const int t = c * kChunk + lane;
+  for (int e = lane; e < E; e += kWave) m[e] = 0ull;
+  __syncthreads();
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[(size_t)t * K + k];
+      if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&m[e]), 1ull << lane);
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) {
+    const uint64_t v = m[e];
+    masks[(size_t)c * E + e] = v;
+    counts[(size_t)c * E + e] = __popcll(v);
+  }
+}
+
+// counts[c][e] -> exclusive prefix over chunks (in place); offsets = exclusive scan over experts.
+__global__ __launch_bounds__(256) void perm_scan_kernel(int E, int nchunks, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets, int tile_rows,
+                                                        int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  __shared__ int32_t tot[kMaxExperts];
+  __shared__ int32_t ntl[kMaxExperts];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    int c = 0;
+    for (; c + 4 <= nchunks; c += 4) {
+      const int v0 = counts[(size_t)(c + 0) * E + e], v1 = counts[(size_t)(c + 1) * E + e];
+      const int v2 = counts[(size_t)(c + 2) * E + e], v3 = counts[(size_t)(c + 3) * E + e];
+      counts[(size_t)(c + 0) * E + e] = run; run += v0;
+      counts[(size_t)(c + 1) * E + e] = run; run += v1;
+      counts[(size_t)(c + 2) * E + e] = run; run += v2;
+      counts[(size_t)(c + 3) * E + e] = run; run += v3;
+    }
+    for (; c < nchunks; ++c) {
+      const int v = counts[(size_t)c * E + e];
+      counts[(size_t)c * E + e] = run;
+      run += v;
+    }
+  }
+  tot[e] = (e < E) ? run : 0;
+  ntl[e] = (e < E && tile_rows > 0) ? (run + tile_rows - 1) / tile_rows : 0;
+  __syncthreads();
+  if (e == 0) {   // E <= 256 sequential adds: negligible next to the chunk loop
+    int acc = 0, tacc = 0;
+    for (int i = 0; i < E; ++i) {
+      const int v = tot[i], n = ntl[i];
+      tot[i] = acc; acc += v;
+      ntl[i] = tacc; tacc += n;
+    }
+    offsets[E] = acc;
+    if (tile_rows > 0) ntiles[0] = tacc;
+  }
+  __syncthreads();
+  if (e < E) {
+    offsets[e] = tot[e];
+    if (tile_rows > 0) {
+      const int nt = (run + tile_rows - 1) / tile_rows;
+      for (int i = 0; i < nt; ++i) {
+        tiles[2 * (ntl[e] + i)] = e;
+        tiles[2 * (ntl[e] + i) + 1] = i * tile_rows;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void perm_scatter_kernel(int T, int E, int K, const int32_t* __restrict__ ids,
+                                                          const uint64_t* __restrict__ masks,
+                                                          const int32_t* __restrict__ base,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_to_row) {
+  const int c = blockIdx.x, lane = threadIdx.x;
+  const int t = c * kChunk + lane;
+  if (t >= T) return;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int k = 0; k < K; ++k) {
+    const int p = t * K + k;
+    const int e = ids[p];
+    if (e < 0 || e >= E) continue;
+    const size_t ce = (size_t)c * E + e;
+    const int row = offsets[e] + base[ce] + __popcll(masks[ce] & below);
+    sorted_pairs[row] = p;
+    pair_to_row[p] = row;
+  }
+}
+
+hipError_t launch_permute(const Shape& s, int T, const int32_t* ids, int nchunks, uint64_t* masks,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
+                          int tile_rows, int32_t* tiles, int32_t* ntiles, hipStream_t stream) {
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(nchunks), dim3(64), 0, stream, T, s.E, s.K, ids, masks, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, stream, s.E, nchunks, counts, offsets, tile_rows,
+                     tiles, ntiles);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nchunks), dim3(64), 0, stream, T, s.E, s.K, ids, masks, counts,
+                     offsets, sorted_pairs, pair_to_row);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -18,7 +18,9 @@ Every tensor comes from its own stream, numpy.random.default_rng(
 [seed, workload_id, tensor_id, index]); tensor ids: 0 x, 1 W_router, 2 bias,
 3 W_gate, 4 W_up, 5 W_down, 6 re-drawn x rows.  Expert matrices are drawn one
 expert at a time, so any single expert can be regenerated on the CPU without
-touching the rest.
+touching the rest.  All real-shape workloads share one layer's expert weights
+(workload id 2 in their seed); the fp8 workloads quantise those same fp32
+draws.
 
 fp32 -> bf16 and fp32 -> e4m3 conversions use torch's CPU casts (round to
 nearest even); they are input preparation, not the layer's arithmetic.
@@ -56,18 +58,19 @@ class Workload:
     sigma_expert: float
     bias: str           # "zero" | "balanced" | "skew"
     weight: str         # "bf16" | "fp8"
+    weights_id: int     # seed id of the expert weights: every real-shape workload shares one layer
 
     def with_T(self, T: int) -> "Workload":
         return replace(self, T=T)
 
 
 def _real(name, wid, T, bias="zero", weight="bf16"):
-    return Workload(name, wid, T, 5120, 2560, 256, 8, 4, 8, 2.5, 0.02, 0.02, bias, weight)
+    return Workload(name, wid, T, 5120, 2560, 256, 8, 4, 8, 2.5, 0.02, 0.02, bias, weight, 2)
 
 
 WORKLOADS = {
     # tiny layer, same routing structure: 32 experts in 8 groups of 4
-    "tiny": Workload("tiny", 1, 64, 256, 128, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "bf16"),
+    "tiny": Workload("tiny", 1, 64, 256, 128, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "bf16", 1),
     # real shape, decode regime: weight streaming
     "decode": _real("decode", 2, 64),
     # real shape, prefill regime with near-balanced expert loads
@@ -200,7 +203,7 @@ def expert_matrix(w: Workload, seed: int, which: str, e: int):
     """
     tid = {"gate": WG_ID, "up": WU_ID, "down": WD_ID}[which]
     shape = (w.inter, w.hidden) if which in ("gate", "up") else (w.hidden, w.inter)
-    a = _rng(seed, w.wid, tid, e).standard_normal(shape, dtype=np.float32)
+    a = _rng(seed, w.weights_id, tid, e).standard_normal(shape, dtype=np.float32)
     a *= np.float32(w.sigma_expert)
     if w.weight == "bf16":
         return bf16_bits(a)
@@ -241,3 +244,44 @@ class ExpertSource:
 
     def drop(self):
         self._cache.clear()
+
+
+def device_expert_weights(w: Workload, seed: int, device, threads: Optional[int] = None, log=None):
+    """All E experts' matrices as device tensors, generated on the host expert by expert.
+
+    Returns dict(gate, up, down) of [E, out, in] tensors (bf16, or uint8 e4m3
+    codes) and, for fp8, s_gate, s_up, s_down [E, out] fp32 scales.
+    """
+    E = w.n_experts
+    fp8 = w.weight == "fp8"
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    out = {"gate": torch.empty(E, w.inter, w.hidden, dtype=wdt, device=device),
+           "up": torch.empty(E, w.inter, w.hidden, dtype=wdt, device=device),
+           "down": torch.empty(E, w.hidden, w.inter, dtype=wdt, device=device)}
+    scales = {}
+    if fp8:
+        scales = {"s_gate": torch.empty(E, w.inter, dtype=torch.float32, device=device),
+                  "s_up": torch.empty(E, w.inter, dtype=torch.float32, device=device),
+                  "s_down": torch.empty(E, w.hidden, dtype=torch.float32, device=device)}
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+
+    def one(key):
+        which, e = key
+        v = expert_matrix(w, seed, which, e)
+        return key, v
+
+    keys = [(wh, e) for e in range(E) for wh in ("gate", "up", "down")]
+    done = 0
+    with ThreadPoolExecutor(threads) as ex:
+        for (which, e), v in ex.map(one, keys):
+            if fp8:
+                q, sc = v
+                out[which][e].copy_(torch.from_numpy(q))
+                scales["s_" + which][e].copy_(torch.from_numpy(sc))
+            else:
+                out[which][e].copy_(torch.from_numpy(v.view(np.int16)).view(torch.bfloat16))
+            done += 1
+            if log and done % 192 == 0:
+                log(f"expert weights: {done}/{len(keys)} matrices")
+    out.update(scales)
+    return out

@@ -1,0 +1,124 @@
+"""The C ABI library: loads, exports every entry point the header declares, and
+rejects invalid arguments before enqueuing anything (no GPU needed: every call
+here fails validation before its first HIP call, or is the T = 0 no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_top_amd as bm
+from sparse_moe_layer_top_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "beam_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(beam_moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("beam_moe_route", "beam_moe_permute", "beam_moe_forward", "beam_moe_workspace_bytes",
+              "beam_moe_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(bm.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert bm.status_string(st) and bm.status_string(st) != "unknown status"
+    assert bm.status_string(7) == "unknown status"
+
+
+def _cfg(**kw):
+    return bm.Config(**kw).c()
+
+
+BAD_CONFIGS = [
+    (dict(n_experts=250), B.ERR_INVALID),                 # E % G != 0
+    (dict(topk_groups=9), B.ERR_INVALID),                 # Gk > G
+    (dict(top_k=0), B.ERR_INVALID),
+    (dict(topk_groups=1, n_groups=64, top_k=8), B.ERR_INVALID),   # K > Gk*E/G = 4
+    (dict(routed_scale=float("inf")), B.ERR_INVALID),
+    (dict(weight_type=3), B.ERR_INVALID),
+    (dict(hidden=5100), B.ERR_UNSUPPORTED),               # not a multiple of 64
+    (dict(n_experts=512, n_groups=8), B.ERR_UNSUPPORTED),
+    (dict(top_k=9, topk_groups=4), B.ERR_UNSUPPORTED),
+    (dict(n_groups=128, n_experts=256, topk_groups=8), B.ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_CONFIGS)
+def test_bad_config_rejected(kw, status):
+    n = ctypes.c_size_t(0)
+    assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg(**kw)), 64, B.OP_FORWARD, ctypes.byref(n)) == status
+    assert B.LIB.beam_moe_route(ctypes.byref(_cfg(**kw)), 64, None, None, None, None, None, None, 0, None) == status
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: each call below fails validation first
+
+
+def test_null_and_negative():
+    c = ctypes.byref(_cfg())
+    assert B.LIB.beam_moe_route(None, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_route(c, -1, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_route(c, B.MAX_TOKENS + 1, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_route(c, 4, None, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_permute(c, 4, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+    args = [FAKE] * 6
+    assert B.LIB.beam_moe_forward(c, 4, None, *args[:5], None, None, None, FAKE, None, None, FAKE, 1 << 30, None) == B.ERR_INVALID
+
+
+def test_misaligned_pointer():
+    c = ctypes.byref(_cfg())
+    odd = ctypes.c_void_p(0x10008)
+    assert B.LIB.beam_moe_route(c, 4, odd, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.ERR_INVALID
+
+
+def test_scale_pointers_must_match_weight_type():
+    c_bf16 = ctypes.byref(_cfg())
+    c_fp8 = ctypes.byref(_cfg(weight_type=B.W_FP8_E4M3))
+    f = FAKE
+    # bf16 with scales, fp8 without: invalid
+    assert B.LIB.beam_moe_forward(c_bf16, 4, f, f, None, f, f, f, f, f, f, f, None, None, f, 1 << 30, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_forward(c_fp8, 4, f, f, None, f, f, f, None, None, None, f, None, None, f, 1 << 30, None) == B.ERR_INVALID
+
+
+def test_workspace_too_small():
+    c = ctypes.byref(_cfg())
+    f = FAKE
+    need = bm.beam_moe_workspace_bytes(bm.Config(), 64, B.OP_ROUTE)
+    assert need > 0
+    assert B.LIB.beam_moe_route(c, 64, f, f, None, f, f, f, need - 1, None) == B.ERR_WORKSPACE
+    assert B.LIB.beam_moe_route(c, 64, f, f, None, f, f, None, need, None) == B.ERR_WORKSPACE
+    need = bm.beam_moe_workspace_bytes(bm.Config(), 64, B.OP_FORWARD)
+    assert B.LIB.beam_moe_forward(c, 64, f, f, None, f, f, f, None, None, None, f, None, None, f, need - 1, None) == B.ERR_WORKSPACE
+    need = bm.beam_moe_workspace_bytes(bm.Config(), 64, B.OP_PERMUTE)
+    assert B.LIB.beam_moe_permute(c, 64, f, f, f, f, f, need - 1, None) == B.ERR_WORKSPACE
+
+
+def test_zero_tokens_is_a_noop():
+    c = ctypes.byref(_cfg())
+    assert B.LIB.beam_moe_route(c, 0, None, None, None, None, None, None, 0, None) == B.OK
+    assert B.LIB.beam_moe_permute(c, 0, None, None, None, None, None, 0, None) == B.OK
+    assert B.LIB.beam_moe_forward(c, 0, *([None] * 13), 0, None) == B.OK
+    assert bm.beam_moe_workspace_bytes(bm.Config(), 0) == 0
+
+
+def test_workspace_grows_with_T():
+    cfg = bm.Config()
+    sizes = [bm.beam_moe_workspace_bytes(cfg, T) for T in (1, 64, 1000, 8192)]
+    assert sizes == sorted(sizes)
+    # forward workspace holds at least h [T*K, I] and y [T*K, H] in bf16
+    assert sizes[-1] >= 8192 * 8 * (2560 + 5120) * 2
+    for op in (B.OP_ROUTE, B.OP_PERMUTE):
+        assert bm.beam_moe_workspace_bytes(cfg, 8192, op) < sizes[-1]

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tiny layer: every step compared in full, several seeds, ragged token counts,
+degenerate routings.  Real shape (hidden 5120, 256 experts, intermediate
+2560): ids, weights and permutation compared in full at the real token counts,
+in the launch configuration the benchmark times, outputs on sampled tokens
+(the oracle computes a token's output from that token alone).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import gen
+from tests import gpu_cases as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import sparse_moe_layer_top_amd  # noqa: F401  (fails loudly if the library is not built)
+    assert torch.cuda.is_available()
+
+
+# ------------------------------------------------------------------ tiny ---
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_tiny_forward_full(seed):
+    w = gen.workload("tiny")
+    spec, x, wr, b = C.guarded(w, seed)
+    W, src = C.host_expert_weights(w, seed)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 63, 64, 65, 130, 257, 1000])
+def test_tiny_ragged_tokens(T):
+    w = gen.workload("tiny", T)
+    spec, x, wr, b = C.guarded(w, 5)
+    W, src = C.host_expert_weights(w, 5)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
+def test_tiny_route_and_permute_entry_points():
+    import sparse_moe_layer_top_amd as bm
+    w = gen.workload("tiny", 333)
+    spec, x, wr, b = C.guarded(w, 2)
+    cfg = C.cfg_of(w)
+    xt, wrt, bt = C.router_tensors(x, wr, b)
+    ids, wts = bm.beam_moe_route(cfg, xt, wrt, bt)
+    off, sp, p2r = bm.beam_moe_permute(cfg, ids)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(spec, x, wr, b)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+    C.check_permutation(rid, off.cpu().numpy(), sp.cpu().numpy(), p2r.cpu().numpy(), w.n_experts)
+    # a NULL bias column is no bias
+    assert len(oracle.gap_violations(spec, x, wr, None)) == 0
+    ids0, w0 = bm.beam_moe_route(cfg, xt, wrt, None)
+    torch.cuda.synchronize()
+    rid0, rw0 = oracle.route(spec, x, wr, None)
+    C.check_ids_w(ids0.cpu().numpy(), w0.cpu().numpy(), rid0, rw0)
+
+
+def test_tiny_all_tokens_same_experts():
+    """A large bias on 8 experts of 2 groups: each of them gets every token (tiles span many rows)."""
+    w = gen.workload("tiny", 300)
+    spec = oracle.LayerSpec.of(w)
+    x, wr, _ = gen.router_inputs(w, 0)
+    b = np.full(w.n_experts, -20.0, np.float32)
+    chosen = [4, 5, 6, 7, 20, 21, 22, 23]
+    b[chosen] = 20.0
+    W, src = C.host_expert_weights(w, 0)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    assert (ref["ids"] == np.array(chosen)).all()
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
+def test_tiny_skewed_bias():
+    w = gen.workload("tiny", 512)
+    spec = oracle.LayerSpec.of(w)
+    bias = (np.random.default_rng(9).standard_normal(w.n_experts) * 1.5).astype(np.float32)
+    x, wr, b, _ = gen.guarded_router_inputs(w, 3, lambda x, wr, b: oracle.gap_violations(spec, x, wr, b), bias=bias)
+    W, src = C.host_expert_weights(w, 3)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    ld = np.bincount(ref["ids"].ravel(), minlength=w.n_experts)
+    assert ld.max() > 2 * ld.mean()
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
+def test_tiny_fp8_weights():
+    w = gen.Workload("tiny_fp8", 1, 96, 256, 128, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "fp8", 1)
+    spec, x, wr, b = C.guarded(w, 4)
+    W, src = C.host_expert_weights(w, 4)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
+def test_tiny_deterministic():
+    w = gen.workload("tiny", 777)
+    spec, x, wr, b = C.guarded(w, 6)
+    W, _ = C.host_expert_weights(w, 6)
+    t = C.router_tensors(x, wr, b)
+    a = C.bits_of(C.run_forward(w, *t, W)[0])
+    c = C.bits_of(C.run_forward(w, *t, W)[0])
+    assert np.array_equal(a, c)
+
+
+def test_zero_tokens():
+    import sparse_moe_layer_top_amd as bm
+    w = gen.workload("tiny")
+    W, _ = C.host_expert_weights(w, 0)
+    x = torch.empty(0, w.hidden, dtype=torch.bfloat16, device=C.dev())
+    wr = torch.zeros(w.hidden, w.n_experts, device=C.dev())
+    out = bm.beam_moe_forward(C.cfg_of(w), x, wr, None, W["gate"], W["up"], W["down"])
+    assert out.shape == (0, w.hidden)
+
+
+def test_permute_max_tokens():
+    """The largest T the ABI accepts: 262144 tokens x 8 slots, random distinct ids per token."""
+    import sparse_moe_layer_top_amd as bm
+    T, E, K = bm.MAX_TOKENS, 256, 8
+    rng = np.random.default_rng(11)
+    ids = np.sort(np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :K], axis=1).astype(np.int32)
+    cfg = bm.Config()
+    off, sp, p2r = bm.beam_moe_permute(cfg, torch.from_numpy(ids).to(C.dev()))
+    torch.cuda.synchronize()
+    C.check_permutation(ids, off.cpu().numpy(), sp.cpu().numpy(), p2r.cpu().numpy(), E)
+
+
+# ------------------------------------------------------------ real shape ---
+
+_WEIGHTS = {}
+
+
+def real_weights(kind):
+    if kind not in _WEIGHTS:
+        w = gen.workload("decode" if kind == "bf16" else "fp8_decode")
+        C.say(f"generating {kind} expert weights (256 experts, real shape)")
+        _WEIGHTS[kind] = gen.device_expert_weights(w, 0, C.dev(), log=C.say)
+    return _WEIGHTS[kind]
+
+
+REAL = [("decode", 8), ("prefill", 4), ("skew", 4), ("fp8_decode", 8), ("fp8_prefill", 4)]
+
+
+@pytest.mark.parametrize("name,n_sample", REAL)
+def test_real_shape_forward(name, n_sample):
+    w = gen.workload(name)
+    C.say(f"[{name}] T={w.T} inputs")
+    spec, x, wr, b = C.guarded(w, 0)
+    W = real_weights(w.weight)
+    C.say(f"[{name}] forward on the GPU")
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    C.say(f"[{name}] oracle routing over all {w.T} tokens")
+    rid, rw = oracle.route(spec, x, wr, b)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+    # outputs of sampled tokens: first, last and a seeded spread
+    rng = np.random.default_rng(1234)
+    sample = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, n_sample, replace=False)]))
+    src = gen.ExpertSource(w, 0)
+    src.prefetch(np.unique(rid[sample]))
+    C.say(f"[{name}] oracle forward on {len(sample)} sampled tokens")
+    ref = oracle.forward(spec, x[sample], wr, b, src.get)
+    assert np.array_equal(ref["ids"], rid[sample])
+    mx, mn = C.check_out(C.bits_of(out)[sample], ref["out"])
+    C.say(f"[{name}] max rel {mx:.2e} mean|d|/rms {mn:.2e}")
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
+def test_real_shape_permute(name):
+    import sparse_moe_layer_top_amd as bm
+    w = gen.workload(name)
+    spec, x, wr, b = C.guarded(w, 0)
+    rid, _ = oracle.route(spec, x, wr, b)
+    off, sp, p2r = bm.beam_moe_permute(C.cfg_of(w), torch.from_numpy(rid).to(C.dev()))
+    torch.cuda.synchronize()
+    C.check_permutation(rid, off.cpu().numpy(), sp.cpu().numpy(), p2r.cpu().numpy(), w.n_experts)
+
+
+def test_real_shape_deterministic():
+    w = gen.workload("decode")
+    spec, x, wr, b = C.guarded(w, 0)
+    W = real_weights("bf16")
+    t = C.router_tensors(x, wr, b)
+    a = C.bits_of(C.run_forward(w, *t, W)[0])
+    c = C.bits_of(C.run_forward(w, *t, W)[0])
+    assert np.array_equal(a, c)

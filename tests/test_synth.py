@@ -31,7 +31,7 @@ def test_fp8_scales_rowmax():
     w = gen.workload("fp8_decode")
     q, s = gen.expert_matrix(w, 0, "gate", 0)
     assert q.dtype == np.uint8 and q.shape == (w.inter, w.hidden) and s.shape == (w.inter,)
-    a = np.random.default_rng([0, w.wid, gen.WG_ID, 0]).standard_normal((w.inter, w.hidden), dtype=np.float32)
+    a = np.random.default_rng([0, w.weights_id, gen.WG_ID, 0]).standard_normal((w.inter, w.hidden), dtype=np.float32)
     a *= np.float32(w.sigma_expert)
     assert np.array_equal(s, (np.abs(a).max(axis=1) / np.float32(448.0)).astype(np.float32))
     assert not np.any((q & 0x7F) == 0x7F)          # no NaN codes
