@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
@@ -109,6 +112,15 @@ def main():
     from synth import gen
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        c = torch.empty_like(a)
+        for _ in range(5):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
     w = gen.workload(args.workload)
     fp8 = w.weight == "fp8"
     cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha,

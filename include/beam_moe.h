@@ -61,8 +61,8 @@ typedef enum { BEAM_MOE_OP_ROUTE = 0, BEAM_MOE_OP_PERMUTE = 1, BEAM_MOE_OP_FORWA
  * Beam's real shape: hidden 5120, inter 2560, 256 experts in 8 groups of 32,
  * 4 kept groups, top-8, alpha 2.5 (overview page, "Mixture of Experts"). */
 typedef struct {
-  int32_t hidden;       /* H: multiple of 64 */
-  int32_t inter;        /* I: multiple of 64 */
+  int32_t hidden;       /* H: multiple of 128 */
+  int32_t inter;        /* I: multiple of 128 */
   int32_t n_experts;    /* E: 1..256 */
   int32_t n_groups;     /* G: 1..64, E % G == 0 */
   int32_t topk_groups;  /* Gk: 1..G */

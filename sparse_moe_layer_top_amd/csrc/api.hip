@@ -29,7 +29,7 @@ int check_config(const beam_moe_config* c) {
   if ((long)c->top_k > (long)c->topk_groups * (c->n_experts / c->n_groups)) return BEAM_MOE_ERR_INVALID;
   if (!isfinite(c->routed_scale)) return BEAM_MOE_ERR_INVALID;
   if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3) return BEAM_MOE_ERR_INVALID;
-  if (c->hidden % 64 != 0 || c->inter % 64 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->n_experts > beam::kMaxExperts || c->n_groups > 64 || c->top_k > beam::kMaxTopK)
     return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;

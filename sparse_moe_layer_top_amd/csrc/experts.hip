@@ -16,92 +16,101 @@
 //
 // FP8 weights (OCP e4m3) are converted exactly to bf16 in registers; the
 // per-output-channel scale multiplies the fp32 accumulator in the epilogue.
+#include <type_traits>
+
 #include "common.h"
 
 namespace beam {
 
 template <bool FP8>
-struct WFrag;   // raw weight fragment of one lane for one k-step: 8 consecutive k of one output row
+struct WFrag;   // one lane's 16-byte weight load per k-step and its conversion to MFMA B-fragments
 template <>
 struct WFrag<false> {
-  using T = bf16x8;
-  static __device__ __forceinline__ T load(const void* base, size_t idx) {
-    return *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(base) + idx);
-  }
-  static __device__ __forceinline__ bf16x8 cvt(T v) { return v; }
+  using E = uint16_t;
+  static constexpr int SK = 32;   // k per step: one 16x16x32 MFMA
+  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int) { return __builtin_bit_cast(bf16x8, v); }
 };
 template <>
 struct WFrag<true> {
-  using T = u32x2;
-  static __device__ __forceinline__ T load(const void* base, size_t idx) {
-    return *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + idx);
+  using E = uint8_t;
+  static constexpr int SK = 64;   // k per step: 16 e4m3 bytes feed two MFMAs
+  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int a) {
+    return e4m3x8_to_bf16x8(a == 0 ? u32x2{v[0], v[1]} : u32x2{v[2], v[3]});
   }
-  static __device__ __forceinline__ bf16x8 cvt(T v) { return e4m3x8_to_bf16x8(v); }
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The streaming k-loop shared by both kernels.  Each k-step of 32 loads NB
-// weight fragments (one per 16-column block, element offsets wofs[nb] + k) and
-// MT activation fragments (arow[mt] + k), and issues MT*NB MFMAs.  Loads run D
-// steps ahead of the MFMAs in a rolling register window, so every wave keeps
-// D*NB weight loads in flight; the window is fully unrolled so each slot is a
-// fixed register set.  Past the end, loads repeat the last step (harmless).
+// The streaming k-loop shared by both kernels.  A step covers SK k-values.
+// Lane (row/column l%16, quad q = l/16) owns k in [step*SK + q*SK/4, +SK/4):
+// one 16-byte weight load per weight block (NB blocks of 16 output columns)
+// and SK/32 16-byte activation loads per row block (MT blocks of 16 rows);
+// wrow/arow already include the lane's quad offset.
+//
+// Loads go out in bursts: a window of D steps is issued back to back (so each
+// weight row sees D*64 contiguous bytes requested together, which HBM serves
+// better than the same loads spread out), and windows are double-buffered:
+// window w+1 is in flight while window w feeds the MFMAs.  sched_barrier
+// fences keep the compiler from reordering the bursts.  nsteps must be a
+// multiple of 2*D (the caller picks D so): a remainder loop after the
+// pipelined one makes the compiler schedule the whole loop worse.
 template <bool FP8, int MT, int NB, int D>
-__device__ __forceinline__ void stream_k(int nsteps, const void* const (&wbase)[NB], const size_t (&wofs)[NB],
+__device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<FP8>::E* const (&wrow)[NB],
                                          const uint16_t* const (&arow)[MT], f32x4 (&acc)[MT][NB]) {
   using W = WFrag<FP8>;
-  typename W::T wb[D][NB];
-  bf16x8 ab[D][MT];
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int st = min(j, nsteps - 1) * 32;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wb[j][nb] = W::load(wbase[nb], wofs[nb] + st);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ab[j][mt] = *reinterpret_cast<const bf16x8*>(arow[mt] + st);
-  }
-  const int nfull = nsteps / D;
-  for (int w = 0; w < nfull; ++w) {
+  constexpr int SK = W::SK, NA = SK / 32;
+  u32x4 wb[2][D][NB];
+  bf16x8 ab[2][D][MT][NA];
+  const int nwin = nsteps / D;
+  auto load = [&](int buf, int w) {
+    const int base = min(w, nwin - 1) * D;   // past the end: reload the last window (unused)
 #pragma unroll
     for (int j = 0; j < D; ++j) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 b = W::cvt(wb[j][nb]);
+      for (int nb = 0; nb < NB; ++nb) wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SK);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][nb] = mfma16(ab[j][mt], b, acc[mt][nb]);
-      }
-      const int st = min((w + 1) * D + j, nsteps - 1) * 32;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wb[j][nb] = W::load(wbase[nb], wofs[nb] + st);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ab[j][mt] = *reinterpret_cast<const bf16x8*>(arow[mt] + st);
+        for (int a = 0; a < NA; ++a)
+          ab[buf][j][mt][a] = *reinterpret_cast<const bf16x8*>(arow[mt] + (base + j) * SK + a * 8);
     }
-  }
-  const int rem = nsteps - nfull * D;   // the last partial window is already loaded
+  };
+  auto compute = [&](int buf) {
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j) {
-    if (j < rem) {
+    for (int j = 0; j < D; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 b = W::cvt(wb[j][nb]);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][nb] = mfma16(ab[j][mt], b, acc[mt][nb]);
-      }
-    }
+        for (int a = 0; a < NA; ++a) {
+          const bf16x8 b = W::frag(wb[buf][j][nb], a);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][nb] = mfma16(ab[buf][j][mt][a], b, acc[mt][nb]);
+        }
+  };
+  load(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int w = 0; w < nwin; w += 2) {
+    load(1, w + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, w + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Prefetch depth (k-steps in flight per wave) by row-tile count.
-template <int MT>
-struct Depth { static constexpr int value = MT == 1 ? 8 : (MT == 2 ? 6 : 4); };
+// Burst depth cap by register budget: 2*D*(NB + MT*SK/32) 16-byte registers per lane.
+template <bool FP8, int MT>
+struct MaxDepth { static constexpr int value = (MT == 1) ? 4 : (MT == 2 ? (FP8 ? 2 : 4) : (FP8 ? 1 : 2)); };
 
 // gate/up: grid (max_tiles, I/64), 4 waves; wave w owns columns [64*by + 16*w, +16) of gate and up.
 // Rows past the tile's end read a valid row (the tile's first) and their
 // outputs are discarded: an MFMA output row depends only on its own A row.
-template <bool FP8, int MT>
+template <bool FP8, int MT, int D>
 __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K, const uint16_t* __restrict__ x,
                                                             const void* __restrict__ wg, const void* __restrict__ wu,
                                                             const float* __restrict__ sg, const float* __restrict__ su,
@@ -110,6 +119,7 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
                                                             const int32_t* __restrict__ tiles,
                                                             const int32_t* __restrict__ ntiles,
                                                             uint16_t* __restrict__ h) {
+  using W = WFrag<FP8>;
   const int tile = blockIdx.x;
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
@@ -118,22 +128,22 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int l16 = lane % 16, q = lane / 16;
   const int col = blockIdx.y * 64 + wave * 16 + l16;
+  const int qk = q * (W::SK / 4);
 
   const uint16_t* xr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
     const int tok = sorted_pairs[lo + r0 + (r < rows ? r : 0)] / K;
-    xr[mt] = x + (size_t)tok * H + q * 8;
+    xr[mt] = x + (size_t)tok * H + qk;
   }
-  // gate and up rows of this lane's column
-  const size_t wrow = ((size_t)e * I + col) * H + q * 8;
-  const void* const wb[2] = {wg, wu};
-  const size_t wofs[2] = {wrow, wrow};
+  using WE = typename W::E;
+  const size_t wrow = ((size_t)e * I + col) * H + qk;
+  const WE* const wr[2] = {static_cast<const WE*>(wg) + wrow, static_cast<const WE*>(wu) + wrow};
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, MT, 2, Depth<MT>::value>(H / 32, wb, wofs, xr, acc);
+  stream_k<FP8, MT, 2, D>(H / W::SK, wr, xr, acc);
 
   float scg = 1.f, scu = 1.f;
   if constexpr (FP8) {
@@ -154,13 +164,14 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
 }
 
 // down: grid (max_tiles, H/128), 4 waves; wave w owns columns [128*by + 32*w, +32) as two 16-col blocks.
-template <bool FP8, int MT>
+template <bool FP8, int MT, int D>
 __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const uint16_t* __restrict__ hbuf,
                                                           const void* __restrict__ wd, const float* __restrict__ sd,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
                                                           uint16_t* __restrict__ y) {
+  using W = WFrag<FP8>;
   const int tile = blockIdx.x;
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
@@ -170,20 +181,21 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
   const int l16 = lane % 16, q = lane / 16;
   const int c0 = blockIdx.y * 128 + wave * 32;
   if (c0 >= H) return;   // wave-uniform; H % 32 == 0 so both 16-column blocks are in range
+  const int qk = q * (W::SK / 4);
 
   const uint16_t* hr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
-    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + q * 8;
+    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + qk;
   }
-  const size_t w0 = ((size_t)e * H + c0 + l16) * I + q * 8;
-  const size_t wofs[2] = {w0, w0 + (size_t)16 * I};
-  const void* const wb[2] = {wd, wd};
+  using WE = typename W::E;
+  const size_t w0 = ((size_t)e * H + c0 + l16) * I + qk;
+  const WE* const wr[2] = {static_cast<const WE*>(wd) + w0, static_cast<const WE*>(wd) + w0 + (size_t)16 * I};
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, MT, 2, Depth<MT>::value>(I / 32, wb, wofs, hr, acc);
+  stream_k<FP8, MT, 2, D>(I / W::SK, wr, hr, acc);
 
   float s0 = 1.f, s1 = 1.f;
   if constexpr (FP8) {
@@ -211,23 +223,41 @@ int expert_tile_rows(const Shape& s, int T) {
   return 64;
 }
 
-template <bool FP8, int MT>
-static hipError_t gateup_mt(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
-                            const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
-                            const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_stream_kernel<FP8, MT>), dim3(max_tiles, s.I / 64), dim3(256), 0, stream, s.H, s.I,
+// Largest D in {4, 2, 1}, at most cap, with nsteps a multiple of 2*D (nsteps is even).
+static int pick_depth(int nsteps, int cap) {
+  for (int d = cap; d > 1; d /= 2)
+    if (nsteps % (2 * d) == 0) return d;
+  return 1;
+}
+
+template <bool FP8, int MT, int D>
+static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
+                                const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                                const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL((gateup_stream_kernel<FP8, MT, D>), dim3(max_tiles, s.I / 64), dim3(256), 0, stream, s.H, s.I,
                      s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h);
   return hipGetLastError();
 }
 
-template <bool FP8, int MT>
-static hipError_t down_mt(const Shape& s, const uint16_t* h, const void* wd, const float* sd, const int32_t* offsets,
-                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* y,
-                          hipStream_t stream) {
-  hipLaunchKernelGGL((down_stream_kernel<FP8, MT>), dim3(max_tiles, (s.H + 127) / 128), dim3(256), 0, stream,
+template <bool FP8, int MT, int D>
+static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
+                              const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                              uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL((down_stream_kernel<FP8, MT, D>), dim3(max_tiles, (s.H + 127) / 128), dim3(256), 0, stream,
                      s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y);
   return hipGetLastError();
+}
+
+// Dispatch on (fp8, row-tile count, depth).
+template <bool FP8, int MT, typename F>
+static hipError_t with_depth(int nsteps, F&& f) {
+  constexpr int cap = MaxDepth<FP8, MT>::value;
+  switch (pick_depth(nsteps, cap)) {
+    case 4: return f(std::integral_constant<int, (cap >= 4 ? 4 : 1)>{});
+    case 2: return f(std::integral_constant<int, (cap >= 2 ? 2 : 1)>{});
+    default: return f(std::integral_constant<int, 1>{});
+  }
 }
 
 hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
@@ -235,20 +265,41 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                          hipStream_t stream) {
   const int bm = expert_tile_rows(s, T);
-#define BEAM_GU(F, M) gateup_mt<F, M>(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream)
-  if (s.fp8) return bm == 16 ? BEAM_GU(true, 1) : bm == 32 ? BEAM_GU(true, 2) : BEAM_GU(true, 4);
-  return bm == 16 ? BEAM_GU(false, 1) : bm == 32 ? BEAM_GU(false, 2) : BEAM_GU(false, 4);
-#undef BEAM_GU
+  auto go = [&](auto fp8, auto mt) {
+    constexpr bool F = decltype(fp8)::value;
+    constexpr int M = decltype(mt)::value;
+    return with_depth<F, M>(s.H / WFrag<F>::SK, [&](auto d) {
+      return gateup_launch<F, M, decltype(d)::value>(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles,
+                                                     max_tiles, h, stream);
+    });
+  };
+  using B = std::bool_constant<false>;
+  using F8 = std::bool_constant<true>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  using M4 = std::integral_constant<int, 4>;
+  if (s.fp8) return bm == 16 ? go(F8{}, M1{}) : bm == 32 ? go(F8{}, M2{}) : go(F8{}, M4{});
+  return bm == 16 ? go(B{}, M1{}) : bm == 32 ? go(B{}, M2{}) : go(B{}, M4{});
 }
 
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        uint16_t* y, hipStream_t stream) {
   const int bm = expert_tile_rows(s, T);
-#define BEAM_DN(F, M) down_mt<F, M>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream)
-  if (s.fp8) return bm == 16 ? BEAM_DN(true, 1) : bm == 32 ? BEAM_DN(true, 2) : BEAM_DN(true, 4);
-  return bm == 16 ? BEAM_DN(false, 1) : bm == 32 ? BEAM_DN(false, 2) : BEAM_DN(false, 4);
-#undef BEAM_DN
+  auto go = [&](auto fp8, auto mt) {
+    constexpr bool F = decltype(fp8)::value;
+    constexpr int M = decltype(mt)::value;
+    return with_depth<F, M>(s.I / WFrag<F>::SK, [&](auto d) {
+      return down_launch<F, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
+    });
+  };
+  using B = std::bool_constant<false>;
+  using F8 = std::bool_constant<true>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  using M4 = std::integral_constant<int, 4>;
+  if (s.fp8) return bm == 16 ? go(F8{}, M1{}) : bm == 32 ? go(F8{}, M2{}) : go(F8{}, M4{});
+  return bm == 16 ? go(B{}, M1{}) : bm == 32 ? go(B{}, M2{}) : go(B{}, M4{});
 }
 
 }  // namespace beam
