@@ -79,4 +79,15 @@ hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float*
 // Rows per grouped-GEMM tile used for the forward's tile list.
 int expert_tile_rows(const Shape& s, int T);
 
+// LDS-tiled expert GEMMs (large token counts): whether T selects them, their tile rows, launchers.
+bool use_tiled(const Shape& s, int T);
+int tiled_tile_rows();
+hipError_t launch_gateup_tiled(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
+                               const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                               hipStream_t stream);
+hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
+                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                             uint16_t* y, hipStream_t stream);
+
 }  // namespace beam

@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
 }
 
 int expert_tile_rows(const Shape& s, int T) {
+  if (use_tiled(s, T)) return tiled_tile_rows();
   const long mean = ((long)T * s.K + s.E - 1) / s.E;
   if (mean <= 12) return 16;
   if (mean <= 28) return 32;
@@ -264,6 +265,8 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
                          const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                          hipStream_t stream) {
+  if (use_tiled(s, T))
+    return launch_gateup_tiled(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
   const int bm = expert_tile_rows(s, T);
   auto go = [&](auto fp8, auto mt) {
     constexpr bool F = decltype(fp8)::value;
@@ -285,6 +288,7 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        uint16_t* y, hipStream_t stream) {
+  if (use_tiled(s, T)) return launch_down_tiled(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
   const int bm = expert_tile_rows(s, T);
   auto go = [&](auto fp8, auto mt) {
     constexpr bool F = decltype(fp8)::value;

@@ -1,0 +1,250 @@
+// Grouped SwiGLU expert GEMMs for large token counts: LDS-tiled bf16 MFMA.
+//
+// Same arithmetic as the weight-streaming kernels (each expert a SwiGLU MLP,
+// Reflection Beam 1.0 overview, section "Mixture of Experts"; the SwiGLU
+// product in FP32, section "Residual stream"), scheduled for the prefill
+// regime where an expert holds hundreds of rows:
+//
+//   * A workgroup owns one row tile of an expert (up to 288 rows, 18 blocks of
+//     16) and 256 weight rows (gate/up: 128 gate + the matching 128 up rows,
+//     so the SwiGLU epilogue stays in registers; down: 256 output columns).
+//     With 288 rows a whole expert of the balanced prefill fits one tile, so
+//     every weight byte comes from HBM once.
+//   * Operands move HBM/L2 -> LDS with direct-to-LDS 16-byte loads
+//     (global_load_lds_dwordx4), laid out fragment-major: fragment f of a stage
+//     is 1 KB, lane l's 16 bytes at f*1KB + l*16, which is exactly what lane l
+//     reads back with one ds_read_b128 for an MFMA operand.  Lane (r = l%16,
+//     quad q = l/16) holds k in [q*16 + 8a, +8) of the 64-wide stage for half
+//     a = 0, 1 (A and B use the same k mapping; the reduction order inside an
+//     MFMA is free).  FP8 weights keep 16 e4m3 bytes per lane (both halves)
+//     and are converted to bf16 when read from LDS.
+//   * Two LDS stages: stage s+1 streams in while stage s feeds the MFMAs.
+//   * 8 waves as 2 (rows) x 4 (columns); a wave owns 9 row blocks x 4 column
+//     blocks of 16x16x32 MFMA accumulators.  Row blocks past the tile's rows
+//     are neither loaded nor multiplied.
+//   * Work items (tile, column block) are dealt to the 8 XCDs in contiguous
+//     ranges, so the workgroups running together on one XCD share the same
+//     expert's activation rows in that XCD's L2.
+#include "common.h"
+
+namespace beam {
+
+constexpr int kTM = 288;            // rows per tile
+constexpr int kTN = 256;            // weight rows per tile
+constexpr int kBK = 64;             // k per LDS stage
+constexpr int kMBlk = kTM / 16;     // 18 row blocks
+constexpr int kNBlk = kTN / 16;     // 16 weight-row blocks
+constexpr int kXcds = 8;
+
+enum { kGateUp = 0, kDown = 1 };
+
+template <bool FP8>
+struct TiledGeom {
+  static constexpr int A_FR = kMBlk * 2;                 // A fragments per stage
+  static constexpr int B_FR = kNBlk * (FP8 ? 1 : 2);     // B fragments per stage
+  static constexpr int FR = A_FR + B_FR;
+  static constexpr int STAGE = FR * 1024;                // bytes per stage
+  static constexpr int LPW = (FR + 7) / 8;               // fragment loads per wave per stage
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const uint16_t* __restrict__ act,
+                                                    const void* __restrict__ w0, const void* __restrict__ w1,
+                                                    const float* __restrict__ s0, const float* __restrict__ s1,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ sorted_pairs,
+                                                    const int32_t* __restrict__ tiles,
+                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out) {
+  using G = TiledGeom<FP8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G::STAGE];
+
+  const int NT = MODE == kGateUp ? I / 128 : H / kTN;     // column blocks per tile
+  const int KD = MODE == kGateUp ? H : I;                 // reduction length
+  const int nitems = ntiles[0] * NT;
+  const int per_xcd = (nitems + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int item = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (item >= nitems) return;
+  const int tile = item / NT, jn = item % NT;
+  const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
+  const int lo = offsets[e];
+  const int rows = min(offsets[e + 1] - lo - r0, kTM);
+  const int nmb = (rows + 15) / 16;
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int l16 = lane % 16, q = lane / 16;
+  const int wm = wave / 4, wn = wave % 4;
+  constexpr int WB = FP8 ? 1 : 2;                          // bytes per weight element
+
+  // the fragments this wave loads every stage: f = wave + 8*i
+  const uint8_t* src[G::LPW];
+  bool on[G::LPW];
+#pragma unroll
+  for (int i = 0; i < G::LPW; ++i) {
+    const int f = wave + 8 * i;
+    on[i] = f < G::FR;
+    src[i] = nullptr;
+    if (!on[i]) continue;
+    if (f < G::A_FR) {
+      const int mb = f / 2, a = f % 2;
+      on[i] = mb < nmb;
+      const int r = min(mb * 16 + l16, rows - 1);
+      const size_t row = MODE == kGateUp ? (size_t)(sorted_pairs[lo + r0 + r] / K) : (size_t)(lo + r0 + r);
+      src[i] = reinterpret_cast<const uint8_t*>(act + row * KD + q * 16 + a * 8);
+    } else {
+      const int fb = f - G::A_FR;
+      const int nb = FP8 ? fb : fb / 2, a = FP8 ? 0 : fb % 2;
+      const void* wbase;
+      size_t wrow;
+      if (MODE == kGateUp) {
+        wbase = nb < 8 ? w0 : w1;
+        wrow = (size_t)e * I + jn * 128 + (nb % 8) * 16 + l16;
+      } else {
+        wbase = w0;
+        wrow = (size_t)e * H + jn * kTN + nb * 16 + l16;
+      }
+      src[i] = static_cast<const uint8_t*>(wbase) + (wrow * KD + q * 16 + a * 8) * WB;
+    }
+  }
+  auto issue = [&](int stage, int buf) {
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+      if (!on[i]) continue;   // wave-uniform
+      const int f = wave + 8 * i;
+      const size_t step = (size_t)stage * kBK * (f < G::A_FR ? 2 : WB);
+      load_lds16(src[i] + step, smem + buf * G::STAGE + f * 1024);
+    }
+  };
+
+  // this wave's weight-row blocks: gate/up pairs for the SwiGLU, or 4 down blocks
+  int nbs[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    nbs[n] = MODE == kGateUp ? ((n < 2) ? 2 * wn + n : 8 + 2 * wn + (n - 2)) : 4 * wn + n;
+
+  f32x4 acc[9][4];
+#pragma unroll
+  for (int m = 0; m < 9; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = KD / kBK;
+  issue(0, 0);
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of stage s have landed
+    __syncthreads();                                    // ... and every other wave's; stage s-1 fully read
+    if (s + 1 < nst) issue(s + 1, buf ^ 1);
+    const uint8_t* st = smem + buf * G::STAGE;
+    u32x4 braw[4];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        braw[n] = *reinterpret_cast<const u32x4*>(st + (G::A_FR + nbs[n]) * 1024 + lane * 16);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        if constexpr (FP8) {
+          b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{braw[n][0], braw[n][1]} : u32x2{braw[n][2], braw[n][3]});
+        } else {
+          b[n] = *reinterpret_cast<const bf16x8*>(st + (G::A_FR + nbs[n] * 2 + a) * 1024 + lane * 16);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 9; ++m) {
+        const int mb = wm * 9 + m;
+        if (mb < nmb) {   // wave-uniform
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + (mb * 2 + a) * 1024 + lane * 16);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block
+  if constexpr (MODE == kGateUp) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int col = jn * 128 + (2 * wn + n) * 16 + l16;
+      const float sg = FP8 ? s0[(size_t)e * I + col] : 1.f;
+      const float su = FP8 ? s1[(size_t)e * I + col] : 1.f;
+#pragma unroll
+      for (int m = 0; m < 9; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = (wm * 9 + m) * 16 + q * 4 + i;
+          if (r < rows) {
+            const float g = acc[m][n][i] * sg, u = acc[m][n + 2][i] * su;
+            out[(size_t)(lo + r0 + r) * I + col] = f32_to_bf16(silu(g) * u);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = jn * kTN + (4 * wn + n) * 16 + l16;
+      const float sd = FP8 ? s0[(size_t)e * H + col] : 1.f;
+#pragma unroll
+      for (int m = 0; m < 9; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = (wm * 9 + m) * 16 + q * 4 + i;
+          if (r < rows) out[(size_t)(lo + r0 + r) * H + col] = f32_to_bf16(acc[m][n][i] * sd);
+        }
+      }
+    }
+  }
+}
+
+bool use_tiled(const Shape& s, int T) {
+  const long mean = ((long)T * s.K) / s.E;
+  return mean >= 32 && s.H % kTN == 0 && s.I % 128 == 0;
+}
+
+int tiled_tile_rows() { return kTM; }
+
+static int grid_for(int max_tiles, int nt) {
+  const long items = (long)max_tiles * nt;
+  return (int)((items + kXcds - 1) / kXcds * kXcds);
+}
+
+hipError_t launch_gateup_tiled(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
+                               const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                               hipStream_t stream) {
+  const dim3 grid(grid_for(max_tiles, s.I / 128));
+  if (s.fp8)
+    hipLaunchKernelGGL((tiled_kernel<kGateUp, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
+                       offsets, sorted_pairs, tiles, ntiles, h);
+  else
+    hipLaunchKernelGGL((tiled_kernel<kGateUp, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
+                       offsets, sorted_pairs, tiles, ntiles, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
+                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                             uint16_t* y, hipStream_t stream) {
+  const dim3 grid(grid_for(max_tiles, s.H / kTN));
+  if (s.fp8)
+    hipLaunchKernelGGL((tiled_kernel<kDown, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
+                       nullptr, offsets, nullptr, tiles, ntiles, y);
+  else
+    hipLaunchKernelGGL((tiled_kernel<kDown, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
+                       nullptr, offsets, nullptr, tiles, ntiles, y);
+  return hipGetLastError();
+}
+
+}  // namespace beam
