@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time the steps without the per-stage events (no roofline entry)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -155,11 +157,12 @@ def main():
     log(f"[bench] timing {steps} steps")
     start.record()
     for i in range(steps):
-        step(evs[i])
+        step(None if args.no_stage_events else evs[i])
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
-    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+    stage_ms = {name: (float("nan") if args.no_stage_events else
+                       float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])))
                 for j, name in enumerate(STAGES)}
 
     # routing statistics and algorithmic work of this batch

@@ -110,9 +110,87 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(int T, int E, int K, c
   }
 }
 
+// Small T (at most kSmallChunks chunks): the three steps in one workgroup of
+// 16 waves, wave w owning chunk w; masks, counts and bases stay in LDS.
+constexpr int kSmallChunks = 16;
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(int T, int E, int K, const int32_t* __restrict__ ids,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ pair_to_row, int tile_rows,
+                                                          int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ ntiles) {
+  __shared__ uint64_t m[kSmallChunks][kMaxExperts];
+  __shared__ int32_t base[kSmallChunks][kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  __shared__ int32_t toff[kMaxExperts];
+  const int tid = threadIdx.x, c = tid / kWave, lane = tid % kWave;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  for (int e = lane; e < E; e += kWave) m[c][e] = 0ull;
+  __syncthreads();
+  const int t = c * kChunk + lane;
+  if (c < nchunks && t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[(size_t)t * K + k];
+      if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&m[c][e]), 1ull << lane);
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) base[c][e] = c < nchunks ? __popcll(m[c][e]) : 0;
+  __syncthreads();
+  int run = 0;
+  if (tid < E) {
+    for (int q = 0; q < nchunks; ++q) {
+      const int v = base[q][tid];
+      base[q][tid] = run;
+      run += v;
+    }
+    off[tid] = run;
+    toff[tid] = tile_rows > 0 ? (run + tile_rows - 1) / tile_rows : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {   // E <= 256 sequential adds
+    int acc = 0, tacc = 0;
+    for (int i = 0; i < E; ++i) {
+      const int v = off[i], n = toff[i];
+      off[i] = acc; acc += v;
+      toff[i] = tacc; tacc += n;
+    }
+    offsets[E] = acc;
+    if (tile_rows > 0) ntiles[0] = tacc;
+  }
+  __syncthreads();
+  if (tid < E) {
+    offsets[tid] = off[tid];
+    if (tile_rows > 0) {
+      const int nt = (run + tile_rows - 1) / tile_rows;
+      for (int i = 0; i < nt; ++i) {
+        tiles[2 * (toff[tid] + i)] = tid;
+        tiles[2 * (toff[tid] + i) + 1] = i * tile_rows;
+      }
+    }
+  }
+  if (c < nchunks && t < T) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int k = 0; k < K; ++k) {
+      const int p = t * K + k;
+      const int e = ids[p];
+      if (e < 0 || e >= E) continue;
+      const int row = off[e] + base[c][e] + __popcll(m[c][e] & below);
+      sorted_pairs[row] = p;
+      pair_to_row[p] = row;
+    }
+  }
+}
+
 hipError_t launch_permute(const Shape& s, int T, const int32_t* ids, int nchunks, uint64_t* masks,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
                           int tile_rows, int32_t* tiles, int32_t* ntiles, hipStream_t stream) {
+  if (nchunks <= kSmallChunks) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, stream, T, s.E, s.K, ids, offsets, sorted_pairs,
+                       pair_to_row, tile_rows, tiles, ntiles);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nchunks), dim3(64), 0, stream, T, s.E, s.K, ids, masks, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -10,8 +10,8 @@
 // Two kernels:
 //   router_logits: z partial sums over a K-split of the hidden dim, fp32 FMA,
 //                  LDS-staged 64-token x 64-expert tiles;
-//   router_select: one wave per token: sum the partials in a fixed order, add
-//                  the bias, sigmoid, then the selection in registers/LDS.
+//   router_select: one workgroup per token: sum the partials in a fixed order,
+//                  add the bias, sigmoid, then the selection in one wave.
 #include "common.h"
 
 namespace beam {
@@ -95,98 +95,100 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// One workgroup per token: thread e sums expert e's K-split partials in a
+// fixed order (coalesced across threads), adds the bias and takes the sigmoid;
+// wave 0 then runs the group-limited selection on the scores in LDS.
 __global__ __launch_bounds__(256) void router_select_kernel(int T, int E, int G, int Gk, int K, int ks,
                                                             float alpha, const float* __restrict__ partial,
                                                             const float* __restrict__ bias,
                                                             int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float s_sc[4][kMaxExperts];
-  __shared__ float s_gs[4][64];
-  __shared__ int s_keep[4][64];
-  __shared__ float s_sel[4][kMaxTopK];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + wave;
-  const bool active = t < T;   // wave-uniform
-  const int gsz = E / G;
-
-  // scores: lane owns experts 4*lane .. 4*lane+3
-  float s[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane * 4 + j;
-    s[j] = -1.f;
-    if (active && e < E) {
-      float z = 0.f;
-      for (int p = 0; p < ks; ++p) z += partial[((size_t)p * T + t) * E + e];
-      if (bias) z += bias[e];
-      s[j] = 1.0f / (1.0f + expf(-z));
-      s_sc[wave][e] = s[j];
-    }
+  __shared__ float s_sc[kMaxExperts];
+  __shared__ float s_gs[64];
+  __shared__ int s_keep[64];
+  __shared__ float s_sel[kMaxTopK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < E) {
+    const float* p = partial + (size_t)t * E + tid;
+    const size_t stride = (size_t)T * E;
+    float z = 0.f;
+    for (int q = 0; q < ks; ++q) z += p[q * stride];
+    if (bias) z += bias[tid];
+    s_sc[tid] = 1.0f / (1.0f + expf(-z));
   }
   __syncthreads();
+  const int lane = tid % kWave;
+  const bool w0 = tid < kWave;   // wave 0 selects; the others only join the barriers
+  const int gsz = E / G;
   // group score = top1 + top2 of the group's scores
-  if (active && lane < G) {
+  if (w0 && lane < G) {
     float a1 = -1.f, a2 = -1.f;
     for (int i = 0; i < gsz; ++i) {
-      const float v = s_sc[wave][lane * gsz + i];
+      const float v = s_sc[lane * gsz + i];
       if (v > a1) { a2 = a1; a1 = v; } else if (v > a2) { a2 = v; }
     }
-    s_gs[wave][lane] = a1 + a2;
+    s_gs[lane] = a1 + a2;
   }
   __syncthreads();
   // keep the Gk best groups (ties: lower group index)
-  if (active && lane < G) {
-    const float mine = s_gs[wave][lane];
+  if (w0 && lane < G) {
+    const float mine = s_gs[lane];
     int rank = 0;
     for (int g = 0; g < G; ++g) {
-      const float o = s_gs[wave][g];
+      const float o = s_gs[g];
       rank += (o > mine) || (o == mine && g < lane);
     }
-    s_keep[wave][lane] = rank < Gk;
+    s_keep[lane] = rank < Gk;
   }
   __syncthreads();
-  bool cand[4], sel[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane * 4 + j;
-    cand[j] = active && e < E && s_keep[wave][e / gsz];
-    sel[j] = false;
-  }
-  // K rounds of a wave-wide argmax over the remaining candidates (ties: lower id)
-  for (int r = 0; r < K; ++r) {
-    uint64_t best = 0;
+  if (w0) {
+    // lane owns experts 4*lane .. 4*lane+3
+    float s[4];
+    bool cand[4], sel[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (cand[j] && !sel[j]) {
-        const uint64_t key = (static_cast<uint64_t>(__float_as_uint(s[j])) << 32) |
-                             (0xFFFFFFFFu - static_cast<uint32_t>(lane * 4 + j));
-        best = key > best ? key : best;
-      }
+      const int e = lane * 4 + j;
+      const bool ok = e < E;
+      s[j] = ok ? s_sc[e] : -1.f;
+      cand[j] = ok && s_keep[e / gsz];
+      sel[j] = false;
     }
-    best = wave_max_u64(best);
-    const uint32_t win = 0xFFFFFFFFu - static_cast<uint32_t>(best);
-    if ((win >> 2) == static_cast<uint32_t>(lane)) sel[win & 3] = true;
-  }
-  // slot of each chosen expert = number of chosen experts with a lower id
-  uint64_t m[4];
+    // K rounds of a wave-wide argmax over the remaining candidates (ties: lower id)
+    for (int r = 0; r < K; ++r) {
+      uint64_t best = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) m[j] = __ballot(sel[j]);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int pos = 0;
+      for (int j = 0; j < 4; ++j) {
+        if (cand[j] && !sel[j]) {
+          const uint64_t key = (static_cast<uint64_t>(__float_as_uint(s[j])) << 32) |
+                               (0xFFFFFFFFu - static_cast<uint32_t>(lane * 4 + j));
+          best = key > best ? key : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const uint32_t win = 0xFFFFFFFFu - static_cast<uint32_t>(best);
+      if ((win >> 2) == static_cast<uint32_t>(lane)) sel[win & 3] = true;
+    }
+    // slot of each chosen expert = number of chosen experts with a lower id
+    uint64_t m[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pos += __popcll(m[j] & below);
+    for (int j = 0; j < 4; ++j) m[j] = __ballot(sel[j]);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int pos = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (sel[j]) {
-      s_sel[wave][pos] = s[j];
-      if (active) ids[(size_t)t * K + pos] = lane * 4 + j;
-      ++pos;
+    for (int j = 0; j < 4; ++j) pos += __popcll(m[j] & below);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sel[j]) {
+        s_sel[pos] = s[j];
+        ids[(size_t)t * K + pos] = lane * 4 + j;
+        ++pos;
+      }
     }
   }
   __syncthreads();
-  if (active && lane < K) {
+  if (w0 && lane < K) {
     float den = 0.f;
-    for (int k = 0; k < K; ++k) den += s_sel[wave][k];   // sequential, ascending expert id
-    wout[(size_t)t * K + lane] = (s_sel[wave][lane] / den) * alpha;
+    for (int k = 0; k < K; ++k) den += s_sel[k];   // sequential, ascending expert id
+    wout[(size_t)t * K + lane] = (s_sel[lane] / den) * alpha;
   }
 }
 
@@ -199,7 +201,7 @@ hipError_t launch_router_logits(const Shape& s, int T, int ks, const uint16_t* x
 
 hipError_t launch_router_select(const Shape& s, int T, int ks, const float* partial, const float* b,
                                 int32_t* ids, float* w, hipStream_t stream) {
-  dim3 grid((T + 3) / 4);
+  dim3 grid(T);
   hipLaunchKernelGGL(router_select_kernel, grid, dim3(256), 0, stream, T, s.E, s.G, s.Gk, s.K, ks, s.alpha,
                      partial, b, ids, w);
   return hipGetLastError();
