@@ -40,7 +40,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("experts.hip", "common.h"):
+    for f in ("experts.hip", "experts_tiled.hip", "common.h"):
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_top_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -181,7 +181,7 @@ def main():
     s = ms / 1e3
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
-    decode_like = TK / w.n_experts < 64
+    decode_like = TK / w.n_experts < 32      # the library's own switch to the LDS-tiled kernels
     t_gu = stage_ms["gateup"] / 1e3
     if decode_like:
         ach = gu_bytes / t_gu / 1e9
@@ -191,7 +191,7 @@ def main():
         ach = gu_flops / t_gu / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    roof["kernel"] = "gateup_stream_kernel"
+    roof["kernel"] = "tiled_kernel<gateup>" if not decode_like else "gateup_stream_kernel"
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["traffic"] = load_traffic(w.name, "gateup")
 
