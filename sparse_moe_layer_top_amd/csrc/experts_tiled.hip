@@ -11,17 +11,23 @@
 //     With 288 rows a whole expert of the balanced prefill fits one tile, so
 //     every weight byte comes from HBM once.
 //   * Operands move HBM/L2 -> LDS with direct-to-LDS 16-byte loads
-//     (global_load_lds_dwordx4), laid out fragment-major: fragment f of a stage
-//     is 1 KB, lane l's 16 bytes at f*1KB + l*16, which is exactly what lane l
-//     reads back with one ds_read_b128 for an MFMA operand.  Lane (r = l%16,
-//     quad q = l/16) holds k in [q*16 + 8a, +8) of the 64-wide stage for half
-//     a = 0, 1 (A and B use the same k mapping; the reduction order inside an
-//     MFMA is free).  FP8 weights keep 16 e4m3 bytes per lane (both halves)
-//     and are converted to bf16 when read from LDS.
+//     (global_load_lds_dwordx4).  One load instruction covers 8 rows x the
+//     row's whole 128-byte stage slice (8 full cache lines): lane l takes row
+//     l/8 and 16-byte chunk (l%8) ^ (l/8) ^ j, j the instruction's half of a
+//     16-row block.  That XOR swizzle lets each lane read its MFMA operand back
+//     with one conflict-free ds_read_b128: lane (r = l%16, q = l/16) of half
+//     a = 0, 1 needs k in [16q + 8a, +8) of the 64-wide stage, i.e. chunk
+//     2q + a of row r.  (Loading 16 rows x 64 bytes per instruction, the
+//     natural fragment order, touches twice the cache lines and halves the
+//     rate at which a CU's loads complete.)  FP8 weights keep 16 e4m3 bytes
+//     per lane (both halves, 16 rows x 64 bytes) and are converted to bf16
+//     when read from LDS; the k mapping is the same.
 //   * Two LDS stages: stage s+1 streams in while stage s feeds the MFMAs.
 //   * 8 waves as 2 (rows) x 4 (columns); a wave owns 9 row blocks x 4 column
 //     blocks of 16x16x32 MFMA accumulators.  Row blocks past the tile's rows
 //     are neither loaded nor multiplied.
+//   * The output tile is staged through LDS and written with 16-byte stores
+//     along rows (whole 128-byte lines), not the MFMA layout's 32-byte pieces.
 //   * Work items (tile, column block) are dealt to the 8 XCDs in contiguous
 //     ranges, so the workgroups running together on one XCD share the same
 //     expert's activation rows in that XCD's L2.
@@ -62,7 +68,10 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
                                                     const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out) {
   using G = TiledGeom<FP8>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * G::STAGE];
+  constexpr int NC = MODE == kGateUp ? 128 : kTN;        // output columns per tile
+  constexpr int CST = NC * 2 + 16;                        // staged output row stride in bytes
+  constexpr int LDS = (2 * G::STAGE > kTM * CST) ? 2 * G::STAGE : kTM * CST;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
   const int NT = MODE == kGateUp ? I / 128 : H / kTN;     // column blocks per tile
   const int KD = MODE == kGateUp ? H : I;                 // reduction length
@@ -82,8 +91,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
   const int l16 = lane % 16, q = lane / 16;
   const int wm = wave / 4, wn = wave % 4;
   constexpr int WB = FP8 ? 1 : 2;                          // bytes per weight element
+  const int lrow = lane / 8, lchunk = (lane % 8) ^ (lane / 8);
 
-  // the fragments this wave loads every stage: f = wave + 8*i
+  // the load instructions this wave issues every stage: f = wave + 8*i
   const uint8_t* src[G::LPW];
   bool on[G::LPW];
 #pragma unroll
@@ -93,24 +103,26 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
     src[i] = nullptr;
     if (!on[i]) continue;
     if (f < G::A_FR) {
-      const int mb = f / 2, a = f % 2;
+      const int mb = f / 2, j = f % 2;
       on[i] = mb < nmb;
-      const int r = min(mb * 16 + l16, rows - 1);
+      const int r = min(mb * 16 + j * 8 + lrow, rows - 1);
       const size_t row = MODE == kGateUp ? (size_t)(sorted_pairs[lo + r0 + r] / K) : (size_t)(lo + r0 + r);
-      src[i] = reinterpret_cast<const uint8_t*>(act + row * KD + q * 16 + a * 8);
+      src[i] = reinterpret_cast<const uint8_t*>(act + row * KD + (lchunk ^ j) * 8);
     } else {
       const int fb = f - G::A_FR;
-      const int nb = FP8 ? fb : fb / 2, a = FP8 ? 0 : fb % 2;
+      const int nb = FP8 ? fb : fb / 2, j = FP8 ? 0 : fb % 2;
+      const int rib = FP8 ? l16 : j * 8 + lrow;            // row inside the 16-row weight block
       const void* wbase;
       size_t wrow;
       if (MODE == kGateUp) {
         wbase = nb < 8 ? w0 : w1;
-        wrow = (size_t)e * I + jn * 128 + (nb % 8) * 16 + l16;
+        wrow = (size_t)e * I + jn * 128 + (nb % 8) * 16 + rib;
       } else {
         wbase = w0;
-        wrow = (size_t)e * H + jn * kTN + nb * 16 + l16;
+        wrow = (size_t)e * H + jn * kTN + nb * 16 + rib;
       }
-      src[i] = static_cast<const uint8_t*>(wbase) + (wrow * KD + q * 16 + a * 8) * WB;
+      const size_t k0 = FP8 ? (size_t)q * 16 : (size_t)(lchunk ^ j) * 8;
+      src[i] = static_cast<const uint8_t*>(wbase) + (wrow * KD + k0) * WB;
     }
   }
   auto issue = [&](int stage, int buf) {
@@ -122,6 +134,11 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
       load_lds16(src[i] + step, smem + buf * G::STAGE + f * 1024);
     }
   };
+
+  // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB load instructions)
+  int roff[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) roff[a] = (l16 / 8) * 1024 + ((l16 % 8) * 8 + ((2 * q + a) ^ (l16 % 8) ^ (l16 / 8))) * 16;
 
   // this wave's weight-row blocks: gate/up pairs for the SwiGLU, or 4 down blocks
   int nbs[4];
@@ -135,12 +152,15 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int kWaitLoads = (7 << 4) | (15 << 8);        // s_waitcnt vmcnt(0)
   const int nst = KD / kBK;
   issue(0, 0);
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of stage s have landed
-    __syncthreads();                                    // ... and every other wave's; stage s-1 fully read
+    __builtin_amdgcn_s_waitcnt(kWaitLoads);             // this wave's loads of stage s have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                       // ... and every other wave's; stage s-1 fully read
+    asm volatile("" ::: "memory");
     if (s + 1 < nst) issue(s + 1, buf ^ 1);
     const uint8_t* st = smem + buf * G::STAGE;
     u32x4 braw[4];
@@ -157,14 +177,14 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
         if constexpr (FP8) {
           b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{braw[n][0], braw[n][1]} : u32x2{braw[n][2], braw[n][3]});
         } else {
-          b[n] = *reinterpret_cast<const bf16x8*>(st + (G::A_FR + nbs[n] * 2 + a) * 1024 + lane * 16);
+          b[n] = *reinterpret_cast<const bf16x8*>(st + (G::A_FR + nbs[n] * 2) * 1024 + roff[a]);
         }
       }
 #pragma unroll
       for (int m = 0; m < 9; ++m) {
         const int mb = wm * 9 + m;
         if (mb < nmb) {   // wave-uniform
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + (mb * 2 + a) * 1024 + lane * 16);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + mb * 2048 + roff[a]);
 #pragma unroll
           for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
         }
@@ -172,21 +192,25 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
     }
   }
 
-  // epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block
+  // epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block; stage the bf16 tile
+  // row-major in LDS (every wave is done with the last stage first), then store whole rows
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if constexpr (MODE == kGateUp) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int col = jn * 128 + (2 * wn + n) * 16 + l16;
-      const float sg = FP8 ? s0[(size_t)e * I + col] : 1.f;
-      const float su = FP8 ? s1[(size_t)e * I + col] : 1.f;
+      const int c = (2 * wn + n) * 16 + l16;
+      const float sg = FP8 ? s0[(size_t)e * I + jn * 128 + c] : 1.f;
+      const float su = FP8 ? s1[(size_t)e * I + jn * 128 + c] : 1.f;
 #pragma unroll
       for (int m = 0; m < 9; ++m) {
+        if (wm * 9 + m < nmb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = (wm * 9 + m) * 16 + q * 4 + i;
-          if (r < rows) {
+          for (int i = 0; i < 4; ++i) {
+            const int r = (wm * 9 + m) * 16 + q * 4 + i;
             const float g = acc[m][n][i] * sg, u = acc[m][n + 2][i] * su;
-            out[(size_t)(lo + r0 + r) * I + col] = f32_to_bf16(silu(g) * u);
+            *reinterpret_cast<uint16_t*>(smem + r * CST + c * 2) = f32_to_bf16(silu(g) * u);
           }
         }
       }
@@ -194,17 +218,27 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
   } else {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const int col = jn * kTN + (4 * wn + n) * 16 + l16;
-      const float sd = FP8 ? s0[(size_t)e * H + col] : 1.f;
+      const int c = (4 * wn + n) * 16 + l16;
+      const float sd = FP8 ? s0[(size_t)e * H + jn * kTN + c] : 1.f;
 #pragma unroll
       for (int m = 0; m < 9; ++m) {
+        if (wm * 9 + m < nmb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = (wm * 9 + m) * 16 + q * 4 + i;
-          if (r < rows) out[(size_t)(lo + r0 + r) * H + col] = f32_to_bf16(acc[m][n][i] * sd);
+          for (int i = 0; i < 4; ++i) {
+            const int r = (wm * 9 + m) * 16 + q * 4 + i;
+            *reinterpret_cast<uint16_t*>(smem + r * CST + c * 2) = f32_to_bf16(acc[m][n][i] * sd);
+          }
         }
       }
     }
+  }
+  __syncthreads();
+  constexpr int CPR = NC / 8;                               // 16-byte chunks per output row
+  const int ldo = MODE == kGateUp ? I : H;
+  uint16_t* const obase = out + (size_t)(lo + r0) * ldo + (size_t)jn * NC;
+  for (int idx = threadIdx.x; idx < rows * CPR; idx += 512) {
+    const int r = idx / CPR, ch = idx % CPR;
+    *reinterpret_cast<u32x4*>(obase + (size_t)r * ldo + ch * 8) = *reinterpret_cast<const u32x4*>(smem + r * CST + ch * 16);
   }
 }
 
