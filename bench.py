@@ -181,19 +181,25 @@ def main():
     s = ms / 1e3
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
-    decode_like = TK / w.n_experts < 32      # the library's own switch to the LDS-tiled kernels
+    tiled = TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0   # the library's switch to the LDS-tiled kernels
     t_gu = stage_ms["gateup"] / 1e3
-    if decode_like:
-        ach = gu_bytes / t_gu / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4)}
+    # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
+    gbps = gu_bytes / t_gu / 1e9
+    tfs = gu_flops / t_gu / 1e12
+    if gu_bytes / (PEAK_HBM_GBPS * 1e9) >= gu_flops / (PEAK_BF16_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     else:
-        ach = gu_flops / t_gu / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    roof["kernel"] = "tiled_kernel<gateup>" if not decode_like else "gateup_stream_kernel"
-    roof["algorithmic_bytes_per_launch"] = gu_bytes
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / PEAK_BF16_TFLOPS, 4)}
     roof["traffic"] = load_traffic(w.name, "gateup")
+    roof["kernel"] = "tiled_kernel<gateup>" if tiled else "gateup_stream_kernel"
+    roof["algorithmic_bytes_per_launch"] = gu_bytes
+    roof["algorithmic_flops_per_launch"] = gu_flops
+    roof["hbm_GBps"] = round(gbps, 1)
+    roof["hbm_frac"] = round(gbps / PEAK_HBM_GBPS, 4)
+    roof["mfma_TFLOPs"] = round(tfs, 1)
+    roof["mfma_frac"] = round(tfs / PEAK_BF16_TFLOPS, 4)
 
     res = {
         "metric": METRIC, "value": round(w.T / s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
