@@ -55,7 +55,12 @@ typedef enum {
 
 typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1 } beam_moe_wtype;
 
-typedef enum { BEAM_MOE_OP_ROUTE = 0, BEAM_MOE_OP_PERMUTE = 1, BEAM_MOE_OP_FORWARD = 2 } beam_moe_op;
+typedef enum {
+  BEAM_MOE_OP_ROUTE = 0,
+  BEAM_MOE_OP_PERMUTE = 1,
+  BEAM_MOE_OP_FORWARD = 2,
+  BEAM_MOE_OP_BLOCK = 3
+} beam_moe_op;
 
 /* Layer configuration (host struct, read at call time).
  * Beam's real shape: hidden 5120, inter 2560, 256 experts in 8 groups of 32,
@@ -73,6 +78,9 @@ typedef struct {
 
 /* Largest T accepted by every entry point. */
 #define BEAM_MOE_MAX_TOKENS 262144
+
+/* Largest hidden size of the norm entry points (a row is staged in 32 KB of LDS). */
+#define BEAM_MOE_MAX_NORM_HIDDEN 16384
 
 /* Static, NUL-terminated description of a status code (host only). */
 const char* beam_moe_status_string(int status);
@@ -145,6 +153,60 @@ int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T,
                            void* out, int32_t* topk_ids_out, float* topk_w_out,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
+
+/* RMSNorm of bf16 rows (the norm before and after every sublayer: Reflection
+ * Beam 1.0 overview, section "Residual stream", which fixes the norms to FP32;
+ * RMSNorm with a per-channel gain is the reading, the only norm the pages name):
+ *   out[t,h] = bf16( (x[t,h] * r_t) * gamma[h] ),  r_t = 1 / sqrt( ss_t / H + eps )
+ * where ss_t is the FP32 sum of x[t,h]^2 over h in index order and every step is
+ * one correctly rounded FP32 operation, so the result is reproducible bit for bit.
+ *   hidden     H: multiple of 8, at most BEAM_MOE_MAX_NORM_HIDDEN
+ *   x          [device] [T, H] bf16
+ *   gamma      [device] [H] fp32 (4-byte aligned)
+ *   eps        finite, > 0
+ *   out        [device] [T, H] bf16 out; may be the same buffer as x
+ * Latency is one sequential H-term FP32 chain per token (tokens run in parallel). */
+int beam_moe_rms_norm(int32_t T, int32_t hidden, const void* x, const float* gamma, float eps, void* out,
+                      void* stream);
+
+/* One MoE sublayer with its norms and Beam's constant-scale residual mix
+ * (overview page, section "Residual stream": the embedding is step 1; at step k
+ * a sublayer's output joins with weight 1/sqrt(k) and the stream keeps weight
+ * sqrt((k-1)/k)):
+ *   x          = RMSNorm(stream_in; gamma_pre, eps)                 (beam_moe_rms_norm)
+ *   moe        = the MoE block on x                                 (beam_moe_forward)
+ *   post       = RMSNorm(moe; gamma_post, eps)
+ *   stream_out = bf16( fp32(a * stream_in) + fp32(b * post) ),  a = fp32(sqrt((k-1)/k)), b = fp32(1/sqrt(k))
+ * The post-norm and the mix run inside the combine kernel.
+ *   cfg, w_router ... s_down   as in beam_moe_forward; hidden <= BEAM_MOE_MAX_NORM_HIDDEN
+ *   step       k >= 2: this sublayer's position in the stream (layer L's MoE sublayer, 0-based L, is 2L+3)
+ *   eps        finite, > 0 (both norms)
+ *   stream_in  [device] [T, H] bf16
+ *   gamma_pre, gamma_post  [device] [H] fp32
+ *   stream_out [device] [T, H] bf16 out; may be the same buffer as stream_in
+ *   moe_out    [device] optional [T, H] bf16 copy of the MoE output before the post-norm (may be NULL)
+ *   topk_ids_out, topk_w_out  [device] optional, as in beam_moe_forward
+ *   workspace  [device] beam_moe_workspace_bytes(BLOCK) bytes (the forward workspace plus x) */
+int beam_moe_block_forward(const beam_moe_config* cfg, int32_t T, int32_t step, float eps,
+                           const void* stream_in, const float* gamma_pre, const float* gamma_post,
+                           const float* w_router, const float* b_router,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           const float* s_gate, const float* s_up, const float* s_down,
+                           void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* beam_moe_block_forward with stage timestamps: stage_events is NULL or 8
+ * hipEvent_t recorded on `stream`:
+ *   0 pre-norm | 1 router logits | 2 router selection | 3 permutation |
+ *   4 gate/up GEMM + SwiGLU | 5 down GEMM | 6 combine + post-norm + mix | 7 end. */
+int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t step, float eps,
+                                 const void* stream_in, const float* gamma_pre, const float* gamma_post,
+                                 const float* w_router, const float* b_router,
+                                 const void* w_gate, const void* w_up, const void* w_down,
+                                 const float* s_gate, const float* s_up, const float* s_down,
+                                 void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events);
 
 #ifdef __cplusplus
 }

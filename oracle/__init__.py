@@ -18,8 +18,11 @@ Parity status of each function:
                                                           reduction)
   moe.forward at the real shape                        -- values are the definition; the
                                                           pages print no worked example
+  block.rms_norm_bits / mix_weights / residual_mix_bits -- pinned (exact-sum bound, closed
+                                                          forms, unit-scale invariants)
+  block.block_forward                                  -- composition of pinned steps
 """
-from . import codecs, moe  # noqa: F401
+from . import block, codecs, moe  # noqa: F401
 from .moe import (  # noqa: F401
     LayerSpec,
     router_logits,
@@ -33,3 +36,4 @@ from .moe import (  # noqa: F401
     combine,
     forward,
 )
+from .block import block_forward, mix_weights, residual_mix_bits, rms_norm_bits  # noqa: F401

@@ -10,14 +10,18 @@ from .binding import (  # noqa: F401
     BeamMoeError,
     Config,
     LIB_PATH,
+    MAX_NORM_HIDDEN,
     MAX_TOKENS,
+    OP_BLOCK,
     OP_FORWARD,
     OP_PERMUTE,
     OP_ROUTE,
     W_BF16,
     W_FP8_E4M3,
+    beam_moe_block_forward,
     beam_moe_forward,
     beam_moe_permute,
+    beam_moe_rms_norm,
     beam_moe_route,
     beam_moe_workspace_bytes,
     status_string,

@@ -18,8 +18,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbeam_mo
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 W_BF16, W_FP8_E4M3 = 0, 1
-OP_ROUTE, OP_PERMUTE, OP_FORWARD = 0, 1, 2
+OP_ROUTE, OP_PERMUTE, OP_FORWARD, OP_BLOCK = 0, 1, 2, 3
 MAX_TOKENS = 262144
+MAX_NORM_HIDDEN = 16384
 
 
 class BeamMoeError(RuntimeError):
@@ -70,6 +71,13 @@ def _load():
     lib.beam_moe_forward.restype = ctypes.c_int
     lib.beam_moe_forward_timed.argtypes = [cfgp, I32] + [P] * 13 + [SZ, P, P]
     lib.beam_moe_forward_timed.restype = ctypes.c_int
+    F32 = ctypes.c_float
+    lib.beam_moe_rms_norm.argtypes = [I32, I32, P, P, F32, P, P]
+    lib.beam_moe_rms_norm.restype = ctypes.c_int
+    lib.beam_moe_block_forward.argtypes = [cfgp, I32, I32, F32] + [P] * 16 + [SZ, P]
+    lib.beam_moe_block_forward.restype = ctypes.c_int
+    lib.beam_moe_block_forward_timed.argtypes = [cfgp, I32, I32, F32] + [P] * 16 + [SZ, P, P]
+    lib.beam_moe_block_forward_timed.restype = ctypes.c_int
     return lib
 
 
@@ -212,3 +220,68 @@ def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_rou
         arr = (ctypes.c_void_p * 7)(*[ev.cuda_event for ev in stage_events])
         _check("beam_moe_forward_timed", LIB.beam_moe_forward_timed(*args, arr))
     return out
+
+
+def beam_moe_rms_norm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out: Optional[torch.Tensor] = None):
+    """RMSNorm of bf16 rows x [T,H] with fp32 gain gamma [H]: bf16((x * r) * gamma), r = 1/sqrt(mean(x^2)+eps),
+    every step one correctly rounded fp32 operation (sum of squares in channel order).  out may be x."""
+    T, H = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(gamma, "gamma", torch.float32, (H,), dev)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _check("beam_moe_rms_norm", LIB.beam_moe_rms_norm(T, H, _ptr(x), _ptr(gamma), ctypes.c_float(eps), _ptr(out),
+                                                      _stream(dev)))
+    return out
+
+
+def beam_moe_block_forward(cfg: Config, step: int, eps: float, stream_in: torch.Tensor, gamma_pre: torch.Tensor,
+                           gamma_post: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor],
+                           w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                           s_gate: Optional[torch.Tensor] = None, s_up: Optional[torch.Tensor] = None,
+                           s_down: Optional[torch.Tensor] = None, stream_out: Optional[torch.Tensor] = None,
+                           moe_out: Optional[torch.Tensor] = None, topk_ids_out: Optional[torch.Tensor] = None,
+                           topk_w_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stage_events=None) -> torch.Tensor:
+    """Pre-norm, the MoE block, post-norm and the constant-scale residual mix at step `step` (>= 2).
+
+    Returns stream_out [T,H] bf16 (may be stream_in itself).  moe_out, if given, receives the MoE output
+    before the post-norm.  stage_events: None or 8 recorded torch.cuda.Event objects."""
+    T, dev = stream_in.shape[0], stream_in.device
+    E, H, I = cfg.n_experts, cfg.hidden, cfg.inter
+    _need(stream_in, "stream_in", torch.bfloat16, (T, H))
+    _need(gamma_pre, "gamma_pre", torch.float32, (H,), dev)
+    _need(gamma_post, "gamma_post", torch.float32, (H,), dev)
+    _need(w_router, "w_router", torch.float32, (H, E), dev)
+    _need(b_router, "b_router", torch.float32, (E,), dev, optional=True)
+    fp8 = cfg.weight_type == W_FP8_E4M3
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(w_gate, "w_gate", wdt, (E, I, H), dev)
+    _need(w_up, "w_up", wdt, (E, I, H), dev)
+    _need(w_down, "w_down", wdt, (E, H, I), dev)
+    _need(s_gate, "s_gate", torch.float32, (E, I), dev, optional=not fp8)
+    _need(s_up, "s_up", torch.float32, (E, I), dev, optional=not fp8)
+    _need(s_down, "s_down", torch.float32, (E, H), dev, optional=not fp8)
+    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
+        raise ValueError("scales are only for fp8 weights")
+    if stream_out is None:
+        stream_out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    _need(stream_out, "stream_out", torch.bfloat16, (T, H), dev)
+    _need(moe_out, "moe_out", torch.bfloat16, (T, H), dev, optional=True)
+    _need(topk_ids_out, "topk_ids_out", torch.int32, (T, cfg.top_k), dev, optional=True)
+    _need(topk_w_out, "topk_w_out", torch.float32, (T, cfg.top_k), dev, optional=True)
+    ws = _workspace(cfg, T, OP_BLOCK, workspace, dev)
+    args = [ctypes.byref(cfg.c()), T, step, ctypes.c_float(eps), _ptr(stream_in), _ptr(gamma_pre), _ptr(gamma_post),
+            _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
+            _ptr(s_down), _ptr(stream_out), _ptr(moe_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+            ws.numel(), _stream(dev)]
+    if stage_events is None:
+        _check("beam_moe_block_forward", LIB.beam_moe_block_forward(*args))
+    else:
+        if len(stage_events) != 8 or any(ev.cuda_event == 0 for ev in stage_events):
+            raise ValueError("stage_events must be 8 torch.cuda.Event objects, each recorded once beforehand")
+        arr = (ctypes.c_void_p * 8)(*[ev.cuda_event for ev in stage_events])
+        _check("beam_moe_block_forward_timed", LIB.beam_moe_block_forward_timed(*args, arr))
+    return stream_out

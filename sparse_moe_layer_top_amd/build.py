@@ -25,6 +25,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every float multiply and add rounds on its own (the oracle's arithmetic);
+    # fused multiply-adds only where the source writes fmaf
+    "-ffp-contract=off",
     "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]

@@ -71,12 +71,13 @@ Layout make_layout(const Shape& s, int T, int op) {
     off = align_up(off + bytes);
     return at;
   };
-  if (op == BEAM_MOE_OP_ROUTE || op == BEAM_MOE_OP_FORWARD) L.logits = take((size_t)L.ks * T * s.E * 4);
-  if (op == BEAM_MOE_OP_PERMUTE || op == BEAM_MOE_OP_FORWARD) {
+  const bool fwd = op == BEAM_MOE_OP_FORWARD || op == BEAM_MOE_OP_BLOCK;
+  if (op == BEAM_MOE_OP_ROUTE || fwd) L.logits = take((size_t)L.ks * T * s.E * 4);
+  if (op == BEAM_MOE_OP_PERMUTE || fwd) {
     L.masks = take((size_t)L.nchunks * s.E * 8);
     L.counts = take((size_t)L.nchunks * s.E * 4);
   }
-  if (op == BEAM_MOE_OP_FORWARD) {
+  if (fwd) {
     L.ids = take(TK * 4);
     L.w = take(TK * 4);
     L.offsets = take((size_t)(s.E + 1) * 4);
@@ -87,6 +88,7 @@ Layout make_layout(const Shape& s, int T, int op) {
     L.h = take(TK * s.I * 2);
     L.y = take(TK * s.H * 2);
   }
+  if (op == BEAM_MOE_OP_BLOCK) L.xn = take((size_t)T * s.H * 2);
   L.total = off;
   return L;
 }
@@ -101,9 +103,78 @@ P* at(void* ws, size_t off) {
     if ((expr) != hipSuccess) return BEAM_MOE_ERR_HIP;   \
   } while (0)
 
+// Checks shared by forward and block (config already checked, T > 0).
+int check_forward_args(const beam_moe_config* cfg, const void* x, const float* w_router, const float* b_router,
+                       const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
+                       const float* s_up, const float* s_down, const void* out, const int32_t* topk_ids_out,
+                       const float* topk_w_out) {
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
+  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
+  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
+    return BEAM_MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(out) || (b_router && !aligned4(b_router)) || (topk_ids_out && !aligned4(topk_ids_out)) ||
+      (topk_w_out && !aligned4(topk_w_out)) || (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+    return BEAM_MOE_ERR_INVALID;
+  return BEAM_MOE_OK;
+}
+
+// The post-norm and residual mix that replace the plain combine in the block path.
+struct BlockEpilogue {
+  float eps, a, b;
+  const float* gamma_post;
+  const uint16_t* stream_in;
+  uint16_t* stream_out;
+  uint16_t* moe_out;   // optional
+};
+
+// Router .. combine on x; `ev` (optional) gets one event before each stage and one after the last.
+int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, const float* w_router,
+                const float* b_router, const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
+                const float* s_up, const float* s_down, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
+                void* workspace, hipStream_t hs, void* const* ev, const BlockEpilogue* blk) {
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
+  float* partial = at<float>(workspace, L.logits);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* p2r = at<int32_t>(workspace, L.p2r);
+  int32_t* tiles = at<int32_t>(workspace, L.tiles);
+  int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
+  uint16_t* h = at<uint16_t>(workspace, L.h);
+  uint16_t* y = at<uint16_t>(workspace, L.y);
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), hs) : hipSuccess;
+  };
+  BEAM_TRY_HIP(mark(0));
+  BEAM_TRY_HIP(beam::launch_router_logits(s, T, L.ks, xb, w_router, partial, hs));
+  BEAM_TRY_HIP(mark(1));
+  BEAM_TRY_HIP(beam::launch_router_select(s, T, L.ks, partial, b_router, ids, w, hs));
+  BEAM_TRY_HIP(mark(2));
+  BEAM_TRY_HIP(beam::launch_permute(s, T, ids, L.nchunks, at<uint64_t>(workspace, L.masks),
+                                    at<int32_t>(workspace, L.counts), offsets, sorted, p2r,
+                                    beam::expert_tile_rows(s, T), tiles, ntiles, hs));
+  BEAM_TRY_HIP(mark(3));
+  BEAM_TRY_HIP(beam::launch_gateup(s, T, xb, w_gate, w_up, s_gate, s_up, offsets, sorted, tiles, ntiles,
+                                   L.max_tiles, h, hs));
+  BEAM_TRY_HIP(mark(4));
+  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, y, hs));
+  BEAM_TRY_HIP(mark(5));
+  if (blk)
+    BEAM_TRY_HIP(beam::launch_combine_norm_mix(s, T, y, w, p2r, blk->eps, blk->gamma_post, blk->a, blk->b,
+                                               blk->stream_in, blk->stream_out, blk->moe_out, hs));
+  else
+    BEAM_TRY_HIP(beam::launch_combine(s, T, y, w, p2r, out, hs));
+  BEAM_TRY_HIP(mark(6));
+  return BEAM_MOE_OK;
+}
+
+bool valid_eps(float eps) { return isfinite(eps) && eps > 0.f; }
+
 }  // namespace
 
 extern "C" {
+
 
 const char* beam_moe_status_string(int status) {
   switch (status) {
@@ -120,7 +191,9 @@ int beam_moe_workspace_bytes(const beam_moe_config* cfg, int32_t T, int32_t op, 
   const int st = check_config(cfg);
   if (st != BEAM_MOE_OK) return st;
   if (!bytes || T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
-  if (op != BEAM_MOE_OP_ROUTE && op != BEAM_MOE_OP_PERMUTE && op != BEAM_MOE_OP_FORWARD) return BEAM_MOE_ERR_INVALID;
+  if (op != BEAM_MOE_OP_ROUTE && op != BEAM_MOE_OP_PERMUTE && op != BEAM_MOE_OP_FORWARD && op != BEAM_MOE_OP_BLOCK)
+    return BEAM_MOE_ERR_INVALID;
+  if (op == BEAM_MOE_OP_BLOCK && cfg->hidden > BEAM_MOE_MAX_NORM_HIDDEN) return BEAM_MOE_ERR_UNSUPPORTED;
   *bytes = T == 0 ? 0 : make_layout(shape_of(cfg), T, op).total;
   return BEAM_MOE_OK;
 }
@@ -182,51 +255,70 @@ int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T, const void* x,
   if (st != BEAM_MOE_OK) return st;
   if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
   if (T == 0) return BEAM_MOE_OK;
-  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
-  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
-  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
-    return BEAM_MOE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      !aligned16(out) || (b_router && !aligned4(b_router)) || (topk_ids_out && !aligned4(topk_ids_out)) ||
-      (topk_w_out && !aligned4(topk_w_out)) || (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
-    return BEAM_MOE_ERR_INVALID;
+  st = check_forward_args(cfg, x, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, out, topk_ids_out,
+                          topk_w_out);
+  if (st != BEAM_MOE_OK) return st;
   const Shape s = shape_of(cfg);
   const Layout L = make_layout(s, T, BEAM_MOE_OP_FORWARD);
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
-  float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
-  float* partial = at<float>(workspace, L.logits);
-  int32_t* offsets = at<int32_t>(workspace, L.offsets);
-  int32_t* sorted = at<int32_t>(workspace, L.sorted);
-  int32_t* p2r = at<int32_t>(workspace, L.p2r);
-  int32_t* tiles = at<int32_t>(workspace, L.tiles);
-  int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
-  uint16_t* h = at<uint16_t>(workspace, L.h);
-  uint16_t* y = at<uint16_t>(workspace, L.y);
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  return run_forward(s, L, T, static_cast<const uint16_t*>(x), w_router, b_router, w_gate, w_up, w_down, s_gate, s_up,
+                     s_down, static_cast<uint16_t*>(out), topk_ids_out, topk_w_out, workspace,
+                     static_cast<hipStream_t>(stream), stage_events, nullptr);
+}
 
-  auto mark = [&](int i) -> hipError_t {
-    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) : hipSuccess;
-  };
-
-  BEAM_TRY_HIP(mark(0));
-  BEAM_TRY_HIP(beam::launch_router_logits(s, T, L.ks, xb, w_router, partial, hs));
-  BEAM_TRY_HIP(mark(1));
-  BEAM_TRY_HIP(beam::launch_router_select(s, T, L.ks, partial, b_router, ids, w, hs));
-  BEAM_TRY_HIP(mark(2));
-  BEAM_TRY_HIP(beam::launch_permute(s, T, ids, L.nchunks, at<uint64_t>(workspace, L.masks),
-                                    at<int32_t>(workspace, L.counts), offsets, sorted, p2r,
-                                    beam::expert_tile_rows(s, T), tiles, ntiles, hs));
-  BEAM_TRY_HIP(mark(3));
-  BEAM_TRY_HIP(beam::launch_gateup(s, T, xb, w_gate, w_up, s_gate, s_up, offsets, sorted, tiles, ntiles,
-                                   L.max_tiles, h, hs));
-  BEAM_TRY_HIP(mark(4));
-  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, y, hs));
-  BEAM_TRY_HIP(mark(5));
-  BEAM_TRY_HIP(beam::launch_combine(s, T, y, w, p2r, static_cast<uint16_t*>(out), hs));
-  BEAM_TRY_HIP(mark(6));
+int beam_moe_rms_norm(int32_t T, int32_t hidden, const void* x, const float* gamma, float eps, void* out,
+                      void* stream) {
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS || hidden <= 0 || hidden % 8 != 0 || !valid_eps(eps))
+    return BEAM_MOE_ERR_INVALID;
+  if (hidden > BEAM_MOE_MAX_NORM_HIDDEN) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_MOE_OK;
+  if (!x || !gamma || !out || !aligned16(x) || !aligned16(out) || !aligned4(gamma)) return BEAM_MOE_ERR_INVALID;
+  BEAM_TRY_HIP(beam::launch_rms_norm(T, hidden, eps, static_cast<const uint16_t*>(x), gamma,
+                                     static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
   return BEAM_MOE_OK;
+}
+
+int beam_moe_block_forward(const beam_moe_config* cfg, int32_t T, int32_t step, float eps, const void* stream_in,
+                           const float* gamma_pre, const float* gamma_post, const float* w_router,
+                           const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+                           const float* s_gate, const float* s_up, const float* s_down, void* stream_out,
+                           void* moe_out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return beam_moe_block_forward_timed(cfg, T, step, eps, stream_in, gamma_pre, gamma_post, w_router, b_router, w_gate,
+                                      w_up, w_down, s_gate, s_up, s_down, stream_out, moe_out, topk_ids_out,
+                                      topk_w_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t step, float eps,
+                                 const void* stream_in, const float* gamma_pre, const float* gamma_post,
+                                 const float* w_router, const float* b_router, const void* w_gate, const void* w_up,
+                                 const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
+                                 void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
+                                 void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
+  int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS || step < 2 || !valid_eps(eps)) return BEAM_MOE_ERR_INVALID;
+  if (cfg->hidden > BEAM_MOE_MAX_NORM_HIDDEN) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_MOE_OK;
+  // the forward's `out` is the block's stream_out; x (the pre-norm output) lives in the workspace
+  st = check_forward_args(cfg, stream_in, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, stream_out,
+                          topk_ids_out, topk_w_out);
+  if (st != BEAM_MOE_OK) return st;
+  if (!gamma_pre || !gamma_post || !aligned4(gamma_pre) || !aligned4(gamma_post) || (moe_out && !aligned16(moe_out)))
+    return BEAM_MOE_ERR_INVALID;
+  const Shape s = shape_of(cfg);
+  const Layout L = make_layout(s, T, BEAM_MOE_OP_BLOCK);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint16_t* xn = at<uint16_t>(workspace, L.xn);
+  if (stage_events) BEAM_TRY_HIP(hipEventRecord(static_cast<hipEvent_t>(stage_events[0]), hs));
+  BEAM_TRY_HIP(beam::launch_rms_norm(T, s.H, eps, static_cast<const uint16_t*>(stream_in), gamma_pre, xn, hs));
+  const BlockEpilogue blk{eps, static_cast<float>(sqrt(static_cast<double>(step - 1) / step)),
+                          static_cast<float>(1.0 / sqrt(static_cast<double>(step))), gamma_post,
+                          static_cast<const uint16_t*>(stream_in), static_cast<uint16_t*>(stream_out),
+                          static_cast<uint16_t*>(moe_out)};
+  return run_forward(s, L, T, xn, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, nullptr,
+                     topk_ids_out, topk_w_out, workspace, hs, stage_events ? stage_events + 1 : nullptr, &blk);
 }
 
 }  // extern "C"

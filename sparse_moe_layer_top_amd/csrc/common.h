@@ -52,7 +52,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ---- workspace carve-up (host) ----
 struct Layout {
-  size_t logits, ids, w, masks, counts, offsets, tiles, ntiles, sorted, p2r, h, y, total;
+  size_t logits, ids, w, masks, counts, offsets, tiles, ntiles, sorted, p2r, h, y, xn, total;
   int ks;        // router k-split
   int nchunks;   // permutation chunks of kChunk tokens
   int max_tiles; // grouped-GEMM row tiles
@@ -75,6 +75,11 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
                        uint16_t* y, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float* w,
                           const int32_t* pair_to_row, uint16_t* out, hipStream_t stream);
+hipError_t launch_rms_norm(int T, int H, float eps, const uint16_t* in, const float* gamma, uint16_t* out,
+                           hipStream_t stream);
+hipError_t launch_combine_norm_mix(const Shape& s, int T, const uint16_t* y, const float* w, const int32_t* pair_to_row,
+                                   float eps, const float* gamma, float a, float b, const uint16_t* stream_in,
+                                   uint16_t* stream_out, uint16_t* moe_out, hipStream_t stream);
 
 // Rows per grouped-GEMM tile used for the forward's tile list.
 int expert_tile_rows(const Shape& s, int T);

@@ -38,7 +38,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
-X_ID, WR_ID, B_ID, WG_ID, WU_ID, WD_ID, REDRAW_ID = 0, 1, 2, 3, 4, 5, 6
+X_ID, WR_ID, B_ID, WG_ID, WU_ID, WD_ID, REDRAW_ID, GAIN_ID = 0, 1, 2, 3, 4, 5, 6, 7
 E4M3_MAX = 448.0
 
 
@@ -190,6 +190,12 @@ def guarded_router_inputs(w: Workload, seed: int,
         n += len(bad)
         x_bits = redraw_rows(x_bits, w, seed, bad, rnd)
     raise RuntimeError(f"gap guard still violated after {max_rounds} re-draw rounds")
+
+
+def norm_gains(w: Workload, seed: int = 0):
+    """Per-channel fp32 gains of the norms before and after the block: 1 + N(0, 0.1^2) each."""
+    g = _rng(seed, w.wid, GAIN_ID).standard_normal((2, w.hidden), dtype=np.float32)
+    return (1.0 + 0.1 * g[0]).astype(np.float32), (1.0 + 0.1 * g[1]).astype(np.float32)
 
 
 # ------------------------------------------------------ expert weights ----

@@ -122,3 +122,61 @@ def test_workspace_grows_with_T():
     assert sizes[-1] >= 8192 * 8 * (2560 + 5120) * 2
     for op in (B.OP_ROUTE, B.OP_PERMUTE):
         assert bm.beam_moe_workspace_bytes(cfg, 8192, op) < sizes[-1]
+
+
+def test_header_declares_norm_and_block_entry_points():
+    names = declared_functions()
+    for n in ("beam_moe_rms_norm", "beam_moe_block_forward", "beam_moe_block_forward_timed"):
+        assert n in names
+
+
+def test_rms_norm_validation():
+    f, g = FAKE, FAKE
+    L = B.LIB
+    assert L.beam_moe_rms_norm(0, 5120, None, None, 1e-6, None, None) == B.OK              # T = 0: no work
+    assert L.beam_moe_rms_norm(-1, 5120, f, g, 1e-6, f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, 5121, f, g, 1e-6, f, None) == B.ERR_INVALID             # not a multiple of 8
+    assert L.beam_moe_rms_norm(4, 0, f, g, 1e-6, f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, 5120, f, g, 0.0, f, None) == B.ERR_INVALID              # eps must be > 0
+    assert L.beam_moe_rms_norm(4, 5120, f, g, float("nan"), f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, 5120, f, g, float("inf"), f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, B.MAX_NORM_HIDDEN + 8, f, g, 1e-6, f, None) == B.ERR_UNSUPPORTED
+    assert L.beam_moe_rms_norm(4, 5120, None, g, 1e-6, f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, 5120, f, None, 1e-6, f, None) == B.ERR_INVALID
+    assert L.beam_moe_rms_norm(4, 5120, ctypes.c_void_p(0x10008), g, 1e-6, f, None) == B.ERR_INVALID
+
+
+def _block(cfg, T, step=5, eps=1e-6, stream_in=FAKE, gpre=FAKE, gpost=FAKE, scales=(None, None, None),
+           stream_out=FAKE, moe_out=None, ws=FAKE, ws_bytes=1 << 40):
+    f = FAKE
+    return B.LIB.beam_moe_block_forward(ctypes.byref(cfg), T, step, eps, stream_in, gpre, gpost, f, None, f, f, f,
+                                        *scales, stream_out, moe_out, None, None, ws, ws_bytes, None)
+
+
+def test_block_validation():
+    c = _cfg()
+    assert _block(c, 0, stream_in=None, gpre=None, gpost=None, stream_out=None, ws=None, ws_bytes=0) == B.OK
+    assert _block(c, 4, step=1) == B.ERR_INVALID                    # the embedding is step 1
+    assert _block(c, 4, eps=0.0) == B.ERR_INVALID
+    assert _block(c, 4, eps=float("nan")) == B.ERR_INVALID
+    assert _block(c, 4, gpre=None) == B.ERR_INVALID
+    assert _block(c, 4, gpost=None) == B.ERR_INVALID
+    assert _block(c, 4, stream_out=None) == B.ERR_INVALID
+    assert _block(c, 4, moe_out=ctypes.c_void_p(0x10008)) == B.ERR_INVALID
+    assert _block(c, 4, scales=(FAKE, FAKE, FAKE)) == B.ERR_INVALID  # bf16 with scales
+    assert _block(_cfg(hidden=16384 + 128), 4) == B.ERR_UNSUPPORTED
+    need = bm.beam_moe_workspace_bytes(bm.Config(), 64, B.OP_BLOCK)
+    assert _block(c, 64, ws_bytes=need - 1) == B.ERR_WORKSPACE
+    assert _block(c, 64, ws=None) == B.ERR_WORKSPACE
+
+
+def test_block_workspace_adds_the_normalised_input():
+    cfg = bm.Config()
+    for T in (1, 64, 8192):
+        fwd = bm.beam_moe_workspace_bytes(cfg, T, B.OP_FORWARD)
+        blk = bm.beam_moe_workspace_bytes(cfg, T, B.OP_BLOCK)
+        assert blk >= fwd + T * cfg.hidden * 2
+    n = ctypes.c_size_t(0)
+    assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=16384 + 128)), 4, B.OP_BLOCK,
+                                          ctypes.byref(n)) == B.ERR_UNSUPPORTED
+    assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg()), 4, 9, ctypes.byref(n)) == B.ERR_INVALID

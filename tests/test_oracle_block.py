@@ -1,0 +1,171 @@
+"""Pins for the oracle's norms and residual mix (oracle/block.py), against what
+the pages and the mathematics fix, not against the oracle's own formula:
+
+  * RMSNorm against an exactly summed (math.fsum) float64 reference, within one
+    bf16 ulp, at magnitudes where eps matters and at a width where H vs H-1 shows;
+  * closed forms for constant rows; exact invariance under power-of-two scaling;
+  * the mix weights' squares sum to one (Reflection Beam 1.0 overview, section
+    "Residual stream"); the mixed stream keeps unit scale for unit-scale inputs;
+    late steps keep the old stream almost unchanged;
+  * planted mistakes in the oracle fail these pins.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import block, codecs
+
+
+def _bf16(a):
+    return codecs.bf16_round_bits(np.asarray(a, np.float32))
+
+
+def _ulp_bf16(x):
+    """Spacing of bf16 values at |x| (for x != 0)."""
+    e = np.floor(np.log2(np.abs(x)))
+    return np.exp2(e - 7)
+
+
+def _exact_rms_norm(v_bits, gamma, eps):
+    v = codecs.bf16_to_f64(v_bits)
+    H = v.shape[-1]
+    ss = np.array([math.fsum(row * row) for row in v.reshape(-1, H)]).reshape(v.shape[:-1])
+    return v / np.sqrt(ss / H + eps)[..., None] * np.asarray(gamma, np.float64)
+
+
+@pytest.mark.parametrize("sigma,eps,H", [(1.0, 1e-6, 64), (1e-3, 1e-6, 64), (1e-3, 1e-5, 256), (3.0, 1e-6, 5120)])
+def test_rms_norm_within_one_ulp_of_exact(sigma, eps, H):
+    rng = np.random.default_rng([7, H])
+    v = _bf16(rng.standard_normal((8, H)) * sigma)
+    g = codecs.bf16_to_f64(_bf16(1.0 + 0.25 * rng.standard_normal(H))).astype(np.float32)
+    got = codecs.bf16_to_f64(oracle.rms_norm_bits(v, g, eps))
+    ref = _exact_rms_norm(v, g, eps)
+    nz = ref != 0
+    assert np.all(np.abs(got[nz] - ref[nz]) <= _ulp_bf16(ref[nz]))
+    assert np.all(got[~nz] == 0)
+
+
+def test_rms_norm_constant_rows_closed_form():
+    H = 256
+    v = _bf16(np.full((2, H), 0.5))
+    g = codecs.bf16_to_f64(_bf16(np.linspace(-2, 2, H))).astype(np.float32)
+    # mean(v^2) = 1/4: eps = 0 gives r = 2 exactly, so out = gamma
+    assert np.array_equal(oracle.rms_norm_bits(v, g, 0.0), np.broadcast_to(_bf16(g), (2, H)))
+    # eps = 3/4 gives r = 1, so out = v * gamma = gamma / 2
+    assert np.array_equal(oracle.rms_norm_bits(v, g, 0.75), np.broadcast_to(_bf16(g / 2), (2, H)))
+
+
+def test_rms_norm_power_of_two_scale_invariance():
+    rng = np.random.default_rng(3)
+    v = _bf16(rng.standard_normal((4, 512)))
+    w = _bf16(codecs.bf16_to_f64(v) * 32.0)        # exact: power-of-two scaling of bf16 values
+    g = np.ones(512, np.float32)
+    assert np.array_equal(oracle.rms_norm_bits(v, g, 0.0), oracle.rms_norm_bits(w, g, 0.0))
+    # and the gain scales the output exactly
+    g4 = np.full(512, 4.0, np.float32)
+    assert np.array_equal(codecs.bf16_to_f64(oracle.rms_norm_bits(v, g4, 1e-6)),
+                          4.0 * codecs.bf16_to_f64(oracle.rms_norm_bits(v, g, 1e-6)))
+
+
+def test_rms_norm_output_has_unit_rms():
+    rng = np.random.default_rng(11)
+    v = _bf16(rng.standard_normal((16, 5120)) * 0.37)
+    out = codecs.bf16_to_f64(oracle.rms_norm_bits(v, np.ones(5120, np.float32), 1e-6))
+    assert np.allclose(np.sqrt((out ** 2).mean(axis=1)), 1.0, atol=2e-3)
+
+
+def test_mix_weights_squares_sum_to_one():
+    for k in range(2, 106):
+        a, b = oracle.mix_weights(k)
+        assert abs(float(a) ** 2 + float(b) ** 2 - 1.0) <= 3 * 2.0 ** -24
+        assert 0 < b <= a or k == 2
+    a2, b2 = oracle.mix_weights(2)
+    assert a2 == b2
+    with pytest.raises(ValueError):
+        oracle.mix_weights(1)
+
+
+def test_mix_keeps_unit_scale_and_weights_the_new_output_less_with_depth():
+    rng = np.random.default_rng(5)
+    H = 5120
+    s = _bf16(rng.standard_normal((8, H)))
+    p = _bf16(rng.standard_normal((8, H)))
+    sv, pv = codecs.bf16_to_f64(s), codecs.bf16_to_f64(p)
+    for k in (2, 3, 10, 105):
+        new = codecs.bf16_to_f64(oracle.residual_mix_bits(s, p, k))
+        rms = np.sqrt((new ** 2).mean(axis=1)) / np.sqrt((sv ** 2).mean(axis=1))
+        assert np.allclose(rms, 1.0, atol=0.03)
+        # least squares: new = a_hat * s + b_hat * p, with a_hat^2 + b_hat^2 = 1 and b_hat = 1/sqrt(k)
+        A = np.stack([sv.ravel(), pv.ravel()], axis=1)
+        coef = np.linalg.lstsq(A, new.ravel(), rcond=None)[0]
+        assert abs(coef[1] - 1 / math.sqrt(k)) < 2e-3 and abs(coef[0] - math.sqrt((k - 1) / k)) < 2e-3
+
+
+def test_mix_of_equal_inputs_is_sum_of_weights():
+    rng = np.random.default_rng(9)
+    s = _bf16(rng.standard_normal((4, 256)))
+    new = codecs.bf16_to_f64(oracle.residual_mix_bits(s, s, 2))
+    ref = math.sqrt(2.0) * codecs.bf16_to_f64(s)
+    nz = ref != 0
+    assert np.all(np.abs(new[nz] - ref[nz]) <= _ulp_bf16(ref[nz]))
+
+
+def test_block_special_cases():
+    spec = oracle.LayerSpec(256, 128, 32, 8, 4, 8, 2.5)
+    from synth import gen
+    w = gen.workload("tiny")
+    x_bits, wr, b = gen.router_inputs(w, 0)
+    weights = lambda which, e: gen.expert_matrix(w, 0, which, e)
+    rng = np.random.default_rng(1)
+    g = (1.0 + 0.1 * rng.standard_normal(256)).astype(np.float32)
+    # zero post-norm gain: the block adds nothing, the stream is only rescaled by a
+    res = oracle.block_forward(spec, x_bits, g, np.zeros(256, np.float32), 1e-6, 7, wr, b, weights)
+    a, _ = oracle.mix_weights(7)
+    assert np.array_equal(res["stream_out"], _bf16(a * codecs.bf16_to_f64(x_bits).astype(np.float32)))
+    # the MoE part sees the pre-norm output
+    assert np.array_equal(res["x"], oracle.rms_norm_bits(x_bits, g, 1e-6))
+    assert np.array_equal(res["out"], oracle.forward(spec, res["x"], wr, b, weights)["out"])
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _eps_outside_sqrt(v_bits, gamma, eps):
+    v = codecs.bf16_to_f64(v_bits).astype(np.float32)
+    r = np.float32(1.0) / (np.sqrt((v * v).mean(axis=-1, dtype=np.float32)) + np.float32(eps))
+    return codecs.bf16_round_bits(v * r[..., None] * np.asarray(gamma, np.float32))
+
+
+def _mean_over_h_minus_1(v_bits, gamma, eps):
+    v = codecs.bf16_to_f64(v_bits).astype(np.float32)
+    H = v.shape[-1]
+    r = np.float32(1.0) / np.sqrt((v * v).sum(axis=-1, dtype=np.float32) / np.float32(H - 1) + np.float32(eps))
+    return codecs.bf16_round_bits(v * r[..., None] * np.asarray(gamma, np.float32))
+
+
+def _no_gain(v_bits, gamma, eps):
+    return block.__dict__["_orig_rms_norm_bits"](v_bits, np.ones_like(np.asarray(gamma, np.float32)), eps)
+
+
+def _swapped_mix_weights(step):
+    a, b = block.__dict__["_orig_mix_weights"](step)
+    return b, a
+
+
+BLOCK_MUTANTS = [
+    ("rms_norm_bits", _eps_outside_sqrt, [lambda: test_rms_norm_within_one_ulp_of_exact(1e-3, 1e-6, 64)]),
+    ("rms_norm_bits", _mean_over_h_minus_1, [lambda: test_rms_norm_within_one_ulp_of_exact(1.0, 1e-6, 64)]),
+    ("rms_norm_bits", _no_gain, [test_rms_norm_constant_rows_closed_form]),
+    ("mix_weights", _swapped_mix_weights, [test_mix_keeps_unit_scale_and_weights_the_new_output_less_with_depth]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", BLOCK_MUTANTS, ids=[f"{m[0]}:{m[1].__name__}" for m in BLOCK_MUTANTS])
+def test_block_mutant_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setitem(block.__dict__, "_orig_" + name, getattr(block, name))
+    monkeypatch.setattr(block, name, mutant)
+    monkeypatch.setattr(oracle, name, mutant)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()
