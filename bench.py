@@ -1,10 +1,12 @@
 """Benchmark of the Beam MoE block forward pass on one MI355X.
 
-    python bench.py [--workload decode|prefill|skew|fp8_decode|fp8_prefill] [--steps K] [--warmup W]
+    python bench.py [--workload decode|prefill|skew|fp8_decode|fp8_prefill] [--steps K] [--warmup W] [--block]
 
 A step is one beam_moe_forward call (router, selection, permutation, gate/up
 GEMM + SwiGLU, down GEMM, combine) over one batch of seeded synthetic inputs
-already resident in HBM.  The timed region is bracketed by device
+already resident in HBM; with --block, one beam_moe_block_forward call (the
+same plus RMSNorm before, and RMSNorm + the constant-scale residual mix fused
+into the combine).  The timed region is bracketed by device
 synchronisation; per-kernel durations come from HIP events that the library
 records on its own stream between stages (beam_moe_forward_timed).
 
@@ -31,6 +33,8 @@ METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MFMA TFLOP/s (prefill) vs pea
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 STAGES = ["router_logits", "router_select", "permute", "gateup", "down", "combine"]
+BLOCK_STAGES = ["pre_norm", "router_logits", "router_select", "permute", "gateup", "down", "combine_norm_mix"]
+BLOCK_STEP, BLOCK_EPS = 23, 1e-6
 DEFAULTS = {"decode": (200, 20), "fp8_decode": (200, 20), "prefill": (30, 5), "skew": (40, 5), "fp8_prefill": (60, 5)}
 
 
@@ -56,7 +60,7 @@ def load_traffic(workload, kernel):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0):
+def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
     """The oracle as it stands, on a bounded token sample of the same workload (host cores)."""
     import oracle
     from synth import gen
@@ -72,10 +76,15 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0):
     start = 0
     while start < w.T and (total_t < seconds_target or total_tok == 0):
         sel = slice(start, min(start + n, w.T))
-        ids, _ = oracle.route(spec, x_bits[sel], wr, b)
+        xs = oracle.rms_norm_bits(x_bits[sel], gen.norm_gains(w, 0)[0], BLOCK_EPS) if block else x_bits[sel]
+        ids, _ = oracle.route(spec, xs, wr, b)
         src.prefetch(np.unique(ids))        # input generation: not timed
         t0 = time.perf_counter()
-        oracle.forward(spec, x_bits[sel], wr, b, src.get)
+        if block:
+            gpre, gpost = gen.norm_gains(w, 0)
+            oracle.block_forward(spec, x_bits[sel], gpre, gpost, BLOCK_EPS, BLOCK_STEP, wr, b, src.get)
+        else:
+            oracle.forward(spec, x_bits[sel], wr, b, src.get)
         total_t += time.perf_counter() - t0
         total_tok += sel.stop - sel.start
         src.drop()
@@ -83,7 +92,8 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0):
         if total_t > seconds_target * 0.5:
             break
     return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), full layer per token, "
+            "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), "
+                      f"{'whole sublayer' if block else 'full layer'} per token, "
                       f"{total_t:.1f} s of oracle time, weight generation excluded"}
 
 
@@ -95,6 +105,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="time the whole sublayer: pre-norm, the MoE block, post-norm and the residual mix "
+                         "(beam_moe_block_forward, step 23 = layer 10's MoE sublayer)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without the per-stage events (no roofline entry)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -140,15 +153,28 @@ def main():
     wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=dev)
     ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
 
+    stages = BLOCK_STAGES if args.block else STAGES
+    if args.block:
+        gpre, gpost = (torch.from_numpy(g).to(dev) for g in gen.norm_gains(w, args.seed))
+        stream_out = torch.empty_like(x)
+        ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T, bm.OP_BLOCK), dtype=torch.uint8, device=dev)
+
     def step(events=None):
-        bm.beam_moe_forward(cfg, x, wr_t, b_t, W["gate"], W["up"], W["down"], W.get("s_gate"), W.get("s_up"),
-                            W.get("s_down"), out=out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
-                            stage_events=events)
+        if args.block:
+            bm.beam_moe_block_forward(cfg, BLOCK_STEP, BLOCK_EPS, x, gpre, gpost, wr_t, b_t, W["gate"], W["up"],
+                                      W["down"], W.get("s_gate"), W.get("s_up"), W.get("s_down"),
+                                      stream_out=stream_out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
+                                      stage_events=events)
+        else:
+            bm.beam_moe_forward(cfg, x, wr_t, b_t, W["gate"], W["up"], W["down"], W.get("s_gate"), W.get("s_up"),
+                                W.get("s_down"), out=out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
+                                stage_events=events)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    nev = len(stages) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     for row in evs:              # record once so each event exists before the library records it
         for e in row:
             e.record()
@@ -163,7 +189,7 @@ def main():
     ms = start.elapsed_time(stop) / steps
     stage_ms = {name: (float("nan") if args.no_stage_events else
                        float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])))
-                for j, name in enumerate(STAGES)}
+                for j, name in enumerate(stages)}
 
     # routing statistics and algorithmic work of this batch
     ids_h = ids.cpu().numpy()
@@ -207,7 +233,9 @@ def main():
         "vs_baseline": None, "dtype": "fp8-e4m3 weights, bf16 MFMA" if fp8 else "bf16",
         "data": "synthetic (seeded, random-init weights of the real layer shape)",
         "config": {"workload": f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
-                               f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}",
+                               f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}"
+                               + (f"; whole sublayer: RMSNorm before and after, residual mix at step {BLOCK_STEP}"
+                                  if args.block else ""),
                    "T": w.T, "weights": w.weight, "bias": w.bias},
         "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
         "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -217,9 +245,17 @@ def main():
                     "zero_load_experts": int((load == 0).sum())},
         "roofline": roof,
     }
+    if args.block:
+        # the two norm kernels: rows read and written (plus the combine's y reads for the fused one)
+        norm_bytes = 2 * w.T * H * 2 + H * 4
+        cnm_bytes = TK * H * 2 + 2 * w.T * H * 2 + H * 4 + TK * 8
+        res["block"] = {"step": BLOCK_STEP, "eps": BLOCK_EPS,
+                        "pre_norm_GBps": round(norm_bytes / (stage_ms["pre_norm"] / 1e3) / 1e9, 1),
+                        "combine_norm_mix_GBps": round(cnm_bytes / (stage_ms["combine_norm_mix"] / 1e3) / 1e9, 1),
+                        "pre_norm_bytes": norm_bytes, "combine_norm_mix_bytes": cnm_bytes}
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(w, x_bits, wr, b)
+        res["cpu_baseline"] = cpu_baseline(w, x_bits, wr, b, block=args.block)
     print(json.dumps(res), flush=True)
 
 

@@ -79,8 +79,8 @@ typedef struct {
 /* Largest T accepted by every entry point. */
 #define BEAM_MOE_MAX_TOKENS 262144
 
-/* Largest hidden size of the norm entry points (a row is staged in 32 KB of LDS). */
-#define BEAM_MOE_MAX_NORM_HIDDEN 16384
+/* Largest hidden size of the norm entry points (a row of fp32 squares is staged in 32 KB of LDS). */
+#define BEAM_MOE_MAX_NORM_HIDDEN 8192
 
 /* Static, NUL-terminated description of a status code (host only). */
 const char* beam_moe_status_string(int status);

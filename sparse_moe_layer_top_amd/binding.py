@@ -20,7 +20,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 W_BF16, W_FP8_E4M3 = 0, 1
 OP_ROUTE, OP_PERMUTE, OP_FORWARD, OP_BLOCK = 0, 1, 2, 3
 MAX_TOKENS = 262144
-MAX_NORM_HIDDEN = 16384
+MAX_NORM_HIDDEN = 8192
 
 
 class BeamMoeError(RuntimeError):

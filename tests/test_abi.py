@@ -164,7 +164,7 @@ def test_block_validation():
     assert _block(c, 4, stream_out=None) == B.ERR_INVALID
     assert _block(c, 4, moe_out=ctypes.c_void_p(0x10008)) == B.ERR_INVALID
     assert _block(c, 4, scales=(FAKE, FAKE, FAKE)) == B.ERR_INVALID  # bf16 with scales
-    assert _block(_cfg(hidden=16384 + 128), 4) == B.ERR_UNSUPPORTED
+    assert _block(_cfg(hidden=8192 + 128), 4) == B.ERR_UNSUPPORTED
     need = bm.beam_moe_workspace_bytes(bm.Config(), 64, B.OP_BLOCK)
     assert _block(c, 64, ws_bytes=need - 1) == B.ERR_WORKSPACE
     assert _block(c, 64, ws=None) == B.ERR_WORKSPACE
@@ -177,6 +177,6 @@ def test_block_workspace_adds_the_normalised_input():
         blk = bm.beam_moe_workspace_bytes(cfg, T, B.OP_BLOCK)
         assert blk >= fwd + T * cfg.hidden * 2
     n = ctypes.c_size_t(0)
-    assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=16384 + 128)), 4, B.OP_BLOCK,
+    assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=8192 + 128)), 4, B.OP_BLOCK,
                                           ctypes.byref(n)) == B.ERR_UNSUPPORTED
     assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg()), 4, 9, ctypes.byref(n)) == B.ERR_INVALID
