@@ -35,7 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 STAGES = ["router_logits", "router_select", "permute", "gateup", "down", "combine"]
 BLOCK_STAGES = ["pre_norm", "router_logits", "router_select", "permute", "gateup", "down", "combine_norm_mix"]
 BLOCK_STEP, BLOCK_EPS = 23, 1e-6
-DEFAULTS = {"decode": (200, 20), "fp8_decode": (200, 20), "prefill": (30, 5), "skew": (40, 5), "fp8_prefill": (60, 5)}
+DEFAULTS = {"decode": (200, 20), "fp8_decode": (200, 20), "prefill": (30, 5), "skew": (40, 5), "fp8_prefill": (60, 5),
+            "spec_verify": (200, 20), "dense_decode": (200, 20), "dense_prefill": (30, 5)}
+DENSE_STAGES = ["setup", "gateup", "down"]
 
 
 def log(msg):
@@ -69,8 +71,21 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
-    spec = oracle.LayerSpec.of(w)
     n = 2 if w.T >= 2 else 1
+    if w.n_experts == 1:                     # dense MLP: generate its three matrices once (not timed)
+        mats = [gen.expert_matrix(w, 0, k, 0) for k in ("gate", "up", "down")]
+        total_t, total_tok = 0.0, 0
+        for start in range(0, w.T, n):
+            t0 = time.perf_counter()
+            oracle.dense_mlp(x_bits[start:start + n], *mats, weight=w.weight)
+            total_t += time.perf_counter() - t0
+            total_tok += min(n, w.T - start)
+            if total_t > seconds_target * 0.5:
+                break
+        return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), dense MLP per token, "
+                          f"{total_t:.1f} s of oracle time, weight generation excluded"}
+    spec = oracle.LayerSpec.of(w)
     src = gen.ExpertSource(w, 0)
     total_t, total_tok = 0.0, 0
     start = 0
@@ -153,14 +168,25 @@ def main():
     wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=dev)
     ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
 
-    stages = BLOCK_STAGES if args.block else STAGES
+    dense = w.n_experts == 1
+    if dense and args.block:
+        print("--block applies to the MoE workloads", file=sys.stderr)
+        sys.exit(2)
+    stages = BLOCK_STAGES if args.block else (DENSE_STAGES if dense else STAGES)
+    if dense:
+        dcfg = bm.DenseConfig(w.hidden, w.inter, bm.W_FP8_E4M3 if fp8 else bm.W_BF16)
+        Wd = {k: v[0] for k, v in W.items()}
+        ws = torch.empty(max(1, bm.beam_dense_workspace_bytes(dcfg, w.T)), dtype=torch.uint8, device=dev)
     if args.block:
         gpre, gpost = (torch.from_numpy(g).to(dev) for g in gen.norm_gains(w, args.seed))
         stream_out = torch.empty_like(x)
         ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T, bm.OP_BLOCK), dtype=torch.uint8, device=dev)
 
     def step(events=None):
-        if args.block:
+        if dense:
+            bm.beam_dense_mlp_forward(dcfg, x, Wd["gate"], Wd["up"], Wd["down"], Wd.get("s_gate"), Wd.get("s_up"),
+                                      Wd.get("s_down"), out=out, workspace=ws, stage_events=events)
+        elif args.block:
             bm.beam_moe_block_forward(cfg, BLOCK_STEP, BLOCK_EPS, x, gpre, gpost, wr_t, b_t, W["gate"], W["up"],
                                       W["down"], W.get("s_gate"), W.get("s_up"), W.get("s_down"),
                                       stream_out=stream_out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
@@ -192,7 +218,7 @@ def main():
                 for j, name in enumerate(stages)}
 
     # routing statistics and algorithmic work of this batch
-    ids_h = ids.cpu().numpy()
+    ids_h = np.zeros((w.T, 1), np.int32) if dense else ids.cpu().numpy()
     load = np.bincount(ids_h.ravel(), minlength=w.n_experts)
     D = int((load > 0).sum())
     TK = w.T * w.top_k
@@ -201,13 +227,16 @@ def main():
     scale_b = 4 if fp8 else 0
     gu_bytes = D * (2 * I * H * wb + 2 * I * scale_b) + w.T * H * 2 + TK * I * 2
     dn_bytes = D * (H * I * wb + H * scale_b) + TK * I * 2 + TK * H * 2
-    layer_bytes = D * (3 * I * H * wb + (2 * I + H) * scale_b) + H * w.n_experts * 4 + w.n_experts * 4 + 2 * w.T * H * 2
+    layer_bytes = D * (3 * I * H * wb + (2 * I + H) * scale_b) + 2 * w.T * H * 2
+    if not dense:
+        layer_bytes += H * w.n_experts * 4 + w.n_experts * 4          # router weights and bias
     layer_flops = 6.0 * TK * H * I
     gu_flops = 4.0 * TK * H * I
     s = ms / 1e3
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
-    tiled = TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0   # the library's switch to the LDS-tiled kernels
+    # the library's switch to the LDS-tiled kernels (the dense path streams up to 1024 tokens)
+    tiled = TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
     gbps = gu_bytes / t_gu / 1e9
@@ -232,8 +261,9 @@ def main():
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8-e4m3 weights, bf16 MFMA" if fp8 else "bf16",
         "data": "synthetic (seeded, random-init weights of the real layer shape)",
-        "config": {"workload": f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
-                               f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}"
+        "config": {"workload": (f"{w.name}: T={w.T}, dense SwiGLU MLP, hidden {H}, inter {I}" if dense else
+                                f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
+                                f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}")
                                + (f"; whole sublayer: RMSNorm before and after, residual mix at step {BLOCK_STEP}"
                                   if args.block else ""),
                    "T": w.T, "weights": w.weight, "bias": w.bias},
@@ -241,8 +271,8 @@ def main():
         "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "layer_bytes": layer_bytes, "layer_flops": layer_flops,
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "routing": {"touched_experts": D, "max_load": int(load.max()), "mean_load": TK / w.n_experts,
-                    "zero_load_experts": int((load == 0).sum())},
+        "routing": None if dense else {"touched_experts": D, "max_load": int(load.max()),
+                                       "mean_load": TK / w.n_experts, "zero_load_experts": int((load == 0).sum())},
         "roofline": roof,
     }
     if args.block:

@@ -208,6 +208,42 @@ int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t 
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* stage_events);
 
+/* Dense SwiGLU MLP: the first 3 of Beam's 52 layers use a dense SwiGLU MLP in
+ * place of the MoE block (overview page, section "Architecture").  The pages do
+ * not give its intermediate size, so it is a parameter.  Same arithmetic as one
+ * expert of the MoE block, for every token, with no router and no combine:
+ *   out[t,:] = bf16( W_down ( bf16( SiLU(W_gate x) * (W_up x) ) ) )
+ * computed by the same grouped-GEMM kernels with one expert. */
+typedef struct {
+  int32_t hidden;       /* H: multiple of 128 */
+  int32_t inter;        /* I: multiple of 128 */
+  int32_t weight_type;  /* beam_moe_wtype */
+} beam_dense_config;
+
+/* Workspace bytes of beam_dense_mlp_forward for T tokens (host only, pure): the
+ * row-tile list, h [T, I] bf16 and, when the down GEMM is split over the
+ * reduction to fill the GPU (small T), its fp32 partial sums. */
+int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* bytes);
+
+/*   x              [device] [T, H] bf16
+ *   w_gate, w_up   [device] [I, H] bf16, or e4m3 bytes with s_gate, s_up [I] fp32
+ *   w_down         [device] [H, I] bf16, or e4m3 bytes with s_down [H] fp32
+ *   out            [device] [T, H] bf16 out
+ *   workspace      [device] beam_dense_workspace_bytes bytes
+ * Deterministic: a split reduction adds its parts in a fixed order. */
+int beam_dense_mlp_forward(const beam_dense_config* cfg, int32_t T, const void* x,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           const float* s_gate, const float* s_up, const float* s_down,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* beam_dense_mlp_forward with stage timestamps: stage_events is NULL or 4
+ * hipEvent_t recorded on `stream`: 0 setup | 1 gate/up GEMM + SwiGLU | 2 down GEMM | 3 end. */
+int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const void* x,
+                                 const void* w_gate, const void* w_up, const void* w_down,
+                                 const float* s_gate, const float* s_up, const float* s_down,
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

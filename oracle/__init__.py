@@ -21,6 +21,8 @@ Parity status of each function:
   block.rms_norm_bits / mix_weights / residual_mix_bits -- pinned (exact-sum bound, closed
                                                           forms, unit-scale invariants)
   block.block_forward                                  -- composition of pinned steps
+  moe.dense_mlp                                        -- pinned (naive loops; equals the
+                                                          MoE layer with identical experts / 2.5)
 """
 from . import block, codecs, moe  # noqa: F401
 from .moe import (  # noqa: F401
@@ -34,6 +36,7 @@ from .moe import (  # noqa: F401
     permute,
     expert_rows,
     combine,
+    dense_mlp,
     forward,
 )
 from .block import block_forward, mix_weights, residual_mix_bits, rms_norm_bits  # noqa: F401

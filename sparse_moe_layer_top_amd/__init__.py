@@ -9,6 +9,7 @@ C ABI of libbeam_moe.so (include/beam_moe.h); every step runs in HIP kernels.
 from .binding import (  # noqa: F401
     BeamMoeError,
     Config,
+    DenseConfig,
     LIB_PATH,
     MAX_NORM_HIDDEN,
     MAX_TOKENS,
@@ -18,6 +19,8 @@ from .binding import (  # noqa: F401
     OP_ROUTE,
     W_BF16,
     W_FP8_E4M3,
+    beam_dense_mlp_forward,
+    beam_dense_workspace_bytes,
     beam_moe_block_forward,
     beam_moe_forward,
     beam_moe_permute,

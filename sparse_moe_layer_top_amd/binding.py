@@ -52,6 +52,21 @@ class Config:
                        self.routed_scale, self.weight_type)
 
 
+class _DenseConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("weight_type", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class DenseConfig:
+    """Dense SwiGLU MLP shape: hidden H, intermediate I (not given on the pages: a parameter)."""
+    hidden: int = 5120
+    inter: int = 20480
+    weight_type: int = W_BF16
+
+    def c(self) -> _DenseConfig:
+        return _DenseConfig(self.hidden, self.inter, self.weight_type)
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run python sparse_moe_layer_top_amd/build.py "
@@ -78,6 +93,13 @@ def _load():
     lib.beam_moe_block_forward.restype = ctypes.c_int
     lib.beam_moe_block_forward_timed.argtypes = [cfgp, I32, I32, F32] + [P] * 16 + [SZ, P, P]
     lib.beam_moe_block_forward_timed.restype = ctypes.c_int
+    dcfgp = ctypes.POINTER(_DenseConfig)
+    lib.beam_dense_workspace_bytes.argtypes = [dcfgp, I32, ctypes.POINTER(SZ)]
+    lib.beam_dense_workspace_bytes.restype = ctypes.c_int
+    lib.beam_dense_mlp_forward.argtypes = [dcfgp, I32] + [P] * 9 + [SZ, P]
+    lib.beam_dense_mlp_forward.restype = ctypes.c_int
+    lib.beam_dense_mlp_forward_timed.argtypes = [dcfgp, I32] + [P] * 9 + [SZ, P, P]
+    lib.beam_dense_mlp_forward_timed.restype = ctypes.c_int
     return lib
 
 
@@ -285,3 +307,49 @@ def beam_moe_block_forward(cfg: Config, step: int, eps: float, stream_in: torch.
         arr = (ctypes.c_void_p * 8)(*[ev.cuda_event for ev in stage_events])
         _check("beam_moe_block_forward_timed", LIB.beam_moe_block_forward_timed(*args, arr))
     return stream_out
+
+
+def beam_dense_workspace_bytes(cfg: DenseConfig, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("beam_dense_workspace_bytes", LIB.beam_dense_workspace_bytes(ctypes.byref(cfg.c()), T, ctypes.byref(n)))
+    return n.value
+
+
+def beam_dense_mlp_forward(cfg: DenseConfig, x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                           w_down: torch.Tensor, s_gate: Optional[torch.Tensor] = None,
+                           s_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stage_events=None) -> torch.Tensor:
+    """Dense SwiGLU MLP: out = bf16(W_down bf16(SiLU(W_gate x) * (W_up x))).  Weights [I,H] / [H,I]: bf16, or
+    uint8 e4m3 codes with fp32 per-output scales.  stage_events: None or 4 recorded torch.cuda.Event objects."""
+    T, dev = x.shape[0], x.device
+    H, I = cfg.hidden, cfg.inter
+    fp8 = cfg.weight_type == W_FP8_E4M3
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(w_gate, "w_gate", wdt, (I, H), dev)
+    _need(w_up, "w_up", wdt, (I, H), dev)
+    _need(w_down, "w_down", wdt, (H, I), dev)
+    _need(s_gate, "s_gate", torch.float32, (I,), dev, optional=not fp8)
+    _need(s_up, "s_up", torch.float32, (I,), dev, optional=not fp8)
+    _need(s_down, "s_down", torch.float32, (H,), dev, optional=not fp8)
+    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
+        raise ValueError("scales are only for fp8 weights")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    need = beam_dense_workspace_bytes(cfg, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 device tensor of at least {need} bytes")
+    args = [ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
+            _ptr(s_down), _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev)]
+    if stage_events is None:
+        _check("beam_dense_mlp_forward", LIB.beam_dense_mlp_forward(*args))
+    else:
+        if len(stage_events) != 4 or any(ev.cuda_event == 0 for ev in stage_events):
+            raise ValueError("stage_events must be 4 torch.cuda.Event objects, each recorded once beforehand")
+        arr = (ctypes.c_void_p * 4)(*[ev.cuda_event for ev in stage_events])
+        _check("beam_dense_mlp_forward_timed", LIB.beam_dense_mlp_forward_timed(*args, arr))
+    return out

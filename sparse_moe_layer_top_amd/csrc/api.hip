@@ -158,7 +158,7 @@ int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, cons
   BEAM_TRY_HIP(beam::launch_gateup(s, T, xb, w_gate, w_up, s_gate, s_up, offsets, sorted, tiles, ntiles,
                                    L.max_tiles, h, hs));
   BEAM_TRY_HIP(mark(4));
-  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, y, hs));
+  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, 1, nullptr, y, hs));
   BEAM_TRY_HIP(mark(5));
   if (blk)
     BEAM_TRY_HIP(beam::launch_combine_norm_mix(s, T, y, w, p2r, blk->eps, blk->gamma_post, blk->a, blk->b,
@@ -167,6 +167,47 @@ int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, cons
     BEAM_TRY_HIP(beam::launch_combine(s, T, y, w, p2r, out, hs));
   BEAM_TRY_HIP(mark(6));
   return BEAM_MOE_OK;
+}
+
+// ---- dense SwiGLU MLP (one expert, every token) ----
+
+int check_dense_config(const beam_dense_config* c) {
+  if (!c || c->hidden <= 0 || c->inter <= 0) return BEAM_MOE_ERR_INVALID;
+  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3) return BEAM_MOE_ERR_INVALID;
+  if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
+  return BEAM_MOE_OK;
+}
+
+Shape dense_shape(const beam_dense_config* c) {
+  Shape s{c->hidden, c->inter, 1, 1, 1, 1, 1.0f, c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
+  s.dense = 1;
+  return s;
+}
+
+struct DenseLayout {
+  size_t offsets, sorted, tiles, ntiles, h, part, total;
+  int max_tiles, tile_rows, kparts;
+};
+
+DenseLayout dense_layout(const Shape& s, int T) {
+  DenseLayout L{};
+  L.tile_rows = beam::expert_tile_rows(s, T);
+  L.max_tiles = (T + L.tile_rows - 1) / L.tile_rows + 1;
+  L.kparts = beam::down_kparts(s, T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.offsets = take(2 * 4);
+  L.sorted = take((size_t)T * 4);
+  L.tiles = take((size_t)L.max_tiles * 8);
+  L.ntiles = take(4);
+  L.h = take((size_t)T * s.I * 2);
+  if (L.kparts > 1) L.part = take((size_t)L.kparts * T * s.H * 4);
+  L.total = off;
+  return L;
 }
 
 bool valid_eps(float eps) { return isfinite(eps) && eps > 0.f; }
@@ -319,6 +360,62 @@ int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t 
                           static_cast<uint16_t*>(moe_out)};
   return run_forward(s, L, T, xn, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, nullptr,
                      topk_ids_out, topk_w_out, workspace, hs, stage_events ? stage_events + 1 : nullptr, &blk);
+}
+
+
+int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* bytes) {
+  const int st = check_dense_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (!bytes || T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  *bytes = T == 0 ? 0 : dense_layout(dense_shape(cfg), T).total;
+  return BEAM_MOE_OK;
+}
+
+int beam_dense_mlp_forward(const beam_dense_config* cfg, int32_t T, const void* x, const void* w_gate,
+                           const void* w_up, const void* w_down, const float* s_gate, const float* s_up,
+                           const float* s_down, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return beam_dense_mlp_forward_timed(cfg, T, x, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
+                                      workspace_bytes, stream, nullptr);
+}
+
+int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const void* x, const void* w_gate,
+                                 const void* w_up, const void* w_down, const float* s_gate, const float* s_up,
+                                 const float* s_down, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream, void* const* stage_events) {
+  int st = check_dense_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (T == 0) return BEAM_MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
+  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
+  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
+    return BEAM_MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) ||
+      (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+    return BEAM_MOE_ERR_INVALID;
+  const Shape s = dense_shape(cfg);
+  const DenseLayout L = dense_layout(s, T);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return BEAM_MOE_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* tiles = at<int32_t>(workspace, L.tiles);
+  int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
+  uint16_t* h = at<uint16_t>(workspace, L.h);
+  float* part = L.kparts > 1 ? at<float>(workspace, L.part) : nullptr;
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) : hipSuccess;
+  };
+  BEAM_TRY_HIP(mark(0));
+  BEAM_TRY_HIP(beam::launch_dense_setup(T, L.tile_rows, offsets, sorted, tiles, ntiles, hs));
+  BEAM_TRY_HIP(mark(1));
+  BEAM_TRY_HIP(beam::launch_gateup(s, T, static_cast<const uint16_t*>(x), w_gate, w_up, s_gate, s_up, offsets, sorted,
+                                   tiles, ntiles, L.max_tiles, h, hs));
+  BEAM_TRY_HIP(mark(2));
+  BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, L.kparts, part,
+                                 static_cast<uint16_t*>(out), hs));
+  BEAM_TRY_HIP(mark(3));
+  return BEAM_MOE_OK;
 }
 
 }  // extern "C"

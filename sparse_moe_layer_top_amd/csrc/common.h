@@ -24,6 +24,7 @@ struct Shape {
   int H, I, E, G, Gk, K;
   float alpha;
   int fp8;
+  int dense = 0;   // one expert holding every token (a dense SwiGLU MLP): no router, no combine
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -72,9 +73,13 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
                          hipStream_t stream);
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                       int kparts, float* part,
                        uint16_t* y, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float* w,
                           const int32_t* pair_to_row, uint16_t* out, hipStream_t stream);
+int down_kparts(const Shape& s, int T);
+hipError_t launch_dense_setup(int T, int tile_rows, int32_t* offsets, int32_t* sorted_pairs, int32_t* tiles,
+                              int32_t* ntiles, hipStream_t stream);
 hipError_t launch_rms_norm(int T, int H, float eps, const uint16_t* in, const float* gamma, uint16_t* out,
                            hipStream_t stream);
 hipError_t launch_combine_norm_mix(const Shape& s, int T, const uint16_t* y, const float* w, const int32_t* pair_to_row,

@@ -164,13 +164,17 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
 }
 
 // down: grid (max_tiles, H/128), 4 waves; wave w owns columns [128*by + 32*w, +32) as two 16-col blocks.
+// With kparts > 1 (grid z), part z covers reduction steps [z*n, (z+1)*n) and
+// writes its raw fp32 sums to part[z][row][col]; splitk_reduce_kernel adds the
+// parts in z order.  Used when one expert's rows are too few to fill the chip.
 template <bool FP8, int MT, int D>
 __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const uint16_t* __restrict__ hbuf,
                                                           const void* __restrict__ wd, const float* __restrict__ sd,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
-                                                          uint16_t* __restrict__ y) {
+                                                          uint16_t* __restrict__ y, int kparts, int nrows,
+                                                          float* __restrict__ part) {
   using W = WFrag<FP8>;
   const int tile = blockIdx.x;
   if (tile >= ntiles[0]) return;
@@ -195,7 +199,27 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, MT, 2, D>(I / W::SK, wr, hr, acc);
+  const int nsteps = I / W::SK / kparts;
+  if (kparts > 1) {
+    const size_t koff = (size_t)blockIdx.z * nsteps * W::SK;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) hr[mt] += koff;
+    const WE* const wk[2] = {wr[0] + koff, wr[1] + koff};
+    stream_k<FP8, MT, 2, D>(nsteps, wk, hr, acc);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + q * 4 + i;
+        if (r < rows) {
+          float* pr = part + ((size_t)blockIdx.z * nrows + lo + r0 + r) * H + c0 + l16;
+          pr[0] = acc[mt][0][i];
+          pr[16] = acc[mt][1][i];
+        }
+      }
+    return;
+  }
+  stream_k<FP8, MT, 2, D>(nsteps, wr, hr, acc);
 
   float s0 = 1.f, s1 = 1.f;
   if constexpr (FP8) {
@@ -244,10 +268,51 @@ static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* w
 template <bool FP8, int MT, int D>
 static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
                               const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
-                              uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL((down_stream_kernel<FP8, MT, D>), dim3(max_tiles, (s.H + 127) / 128), dim3(256), 0, stream,
-                     s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y);
+                              uint16_t* y, int kparts, int nrows, float* part, hipStream_t stream) {
+  hipLaunchKernelGGL((down_stream_kernel<FP8, MT, D>), dim3(max_tiles, (s.H + 127) / 128, kparts), dim3(256), 0,
+                     stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part);
   return hipGetLastError();
+}
+
+// y[row][col] = bf16( (part[0] + part[1] + ... + part[kparts-1]) * scale[col] ), parts added in order.
+// One expert (the dense path): the fp8 scale of output column col is sd[col].
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int nrows, int H, int kparts, const float* __restrict__ part,
+                                                            const float* __restrict__ sd, uint16_t* __restrict__ y) {
+  const size_t n = (size_t)nrows * H;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (size_t)gridDim.x * 256 * 4) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+    for (int z = 1; z < kparts; ++z) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)z * n + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __fadd_rn(acc[j], v[j]);
+    }
+    u32x2 o;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = (int)((i + 2 * j) % H);
+      const float a = sd ? __fmul_rn(acc[2 * j], sd[c]) : acc[2 * j];
+      const float b = sd ? __fmul_rn(acc[2 * j + 1], sd[c + 1]) : acc[2 * j + 1];
+      o[j] = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    }
+    *reinterpret_cast<u32x2*>(y + i) = o;
+  }
+}
+
+// Reduction parts for the dense path's down GEMM: the fewest parts (a divisor
+// of the step count / 8, so each part keeps the deepest burst schedule) that
+// give about 1024 workgroups; 1 when the row tiles alone do.
+int down_kparts(const Shape& s, int T) {
+  if (!s.dense || use_tiled(s, T)) return 1;
+  const int bm = expert_tile_rows(s, T);
+  const long wgs = (long)((T + bm - 1) / bm) * ((s.H + 127) / 128);
+  const int units = s.I / WFrag<false>::SK / 8 / (s.fp8 ? 2 : 1);   // steps / 8 for the weight type
+  int best = 1;
+  for (int k = 1; k <= 32 && k <= units; ++k) {
+    if (units % k) continue;
+    best = k;
+    if (wgs * k >= 1024) break;
+  }
+  return best;
 }
 
 // Dispatch on (fp8, row-tile count, depth).
@@ -287,15 +352,22 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
 
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
-                       uint16_t* y, hipStream_t stream) {
+                       int kparts, float* part, uint16_t* y, hipStream_t stream) {
   if (use_tiled(s, T)) return launch_down_tiled(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
   const int bm = expert_tile_rows(s, T);
+  const int nrows = T * s.K;
   auto go = [&](auto fp8, auto mt) {
     constexpr bool F = decltype(fp8)::value;
     constexpr int M = decltype(mt)::value;
-    return with_depth<F, M>(s.I / WFrag<F>::SK, [&](auto d) {
-      return down_launch<F, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
+    hipError_t err = with_depth<F, M>(s.I / WFrag<F>::SK / kparts, [&](auto d) {
+      return down_launch<F, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, kparts, nrows,
+                                                   part, stream);
     });
+    if (err != hipSuccess || kparts == 1) return err;
+    const size_t n4 = (size_t)nrows * s.H / 4;
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, nrows, s.H, kparts, part, sd, y);
+    return hipGetLastError();
   };
   using B = std::bool_constant<false>;
   using F8 = std::bool_constant<true>;
@@ -304,6 +376,35 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
   using M4 = std::integral_constant<int, 4>;
   if (s.fp8) return bm == 16 ? go(F8{}, M1{}) : bm == 32 ? go(F8{}, M2{}) : go(F8{}, M4{});
   return bm == 16 ? go(B{}, M1{}) : bm == 32 ? go(B{}, M2{}) : go(B{}, M4{});
+}
+
+}  // namespace beam
+
+namespace beam {
+
+// Identity permutation and row tiles of the single expert of the dense path.
+__global__ __launch_bounds__(256) void dense_setup_kernel(int T, int tile_rows, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pairs,
+                                                          int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int nt = (T + tile_rows - 1) / tile_rows;
+  if (i < T) sorted_pairs[i] = i;
+  if (i < nt) {
+    tiles[2 * i] = 0;
+    tiles[2 * i + 1] = i * tile_rows;
+  }
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+    ntiles[0] = nt;
+  }
+}
+
+hipError_t launch_dense_setup(int T, int tile_rows, int32_t* offsets, int32_t* sorted_pairs, int32_t* tiles,
+                              int32_t* ntiles, hipStream_t stream) {
+  hipLaunchKernelGGL(dense_setup_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, T, tile_rows, offsets,
+                     sorted_pairs, tiles, ntiles);
+  return hipGetLastError();
 }
 
 }  // namespace beam

@@ -243,6 +243,9 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
 }
 
 bool use_tiled(const Shape& s, int T) {
+  // a single expert gives the tiled kernels only ceil(T/288) row tiles: below ~1k
+  // tokens the streaming kernels (64-row tiles, k-split down) fill the chip better
+  if (s.dense && T <= 1024) return false;
   const long mean = ((long)T * s.K) / s.E;
   return mean >= 32 && s.H % kTN == 0 && s.I % 128 == 0;
 }

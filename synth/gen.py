@@ -80,6 +80,13 @@ WORKLOADS = {
     # real shape, e4m3 expert weights + per-output-channel fp32 scales
     "fp8_decode": _real("fp8_decode", 5, 32, weight="fp8"),
     "fp8_prefill": _real("fp8_prefill", 5, 2048, weight="fp8"),
+    # speculative verification: 8 sequences x (1 + 15 drafted tokens) in one forward pass
+    "spec_verify": _real("spec_verify", 6, 128),
+    # dense SwiGLU MLP (the first layers): one "expert" of intermediate 20480 = 8 x 2560
+    # (the pages do not give the dense width; this one does a routed layer's per-token work)
+    "dense_tiny": Workload("dense_tiny", 7, 64, 256, 512, 1, 1, 1, 1, 1.0, 0.05, 0.02, "zero", "bf16", 7),
+    "dense_decode": Workload("dense_decode", 8, 64, 5120, 20480, 1, 1, 1, 1, 1.0, 0.02, 0.02, "zero", "bf16", 8),
+    "dense_prefill": Workload("dense_prefill", 9, 8192, 5120, 20480, 1, 1, 1, 1, 1.0, 0.02, 0.02, "zero", "bf16", 8),
 }
 
 

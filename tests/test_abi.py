@@ -180,3 +180,35 @@ def test_block_workspace_adds_the_normalised_input():
     assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=8192 + 128)), 4, B.OP_BLOCK,
                                           ctypes.byref(n)) == B.ERR_UNSUPPORTED
     assert B.LIB.beam_moe_workspace_bytes(ctypes.byref(_cfg()), 4, 9, ctypes.byref(n)) == B.ERR_INVALID
+
+
+def _dcfg(**kw):
+    return bm.DenseConfig(**kw).c()
+
+
+def test_dense_validation():
+    L = B.LIB
+    f = FAKE
+    c = ctypes.byref(_dcfg())
+    n = ctypes.c_size_t(0)
+    assert L.beam_dense_workspace_bytes(ctypes.byref(_dcfg(hidden=5100)), 4, ctypes.byref(n)) == B.ERR_UNSUPPORTED
+    assert L.beam_dense_workspace_bytes(ctypes.byref(_dcfg(inter=0)), 4, ctypes.byref(n)) == B.ERR_INVALID
+    assert L.beam_dense_workspace_bytes(ctypes.byref(_dcfg(weight_type=5)), 4, ctypes.byref(n)) == B.ERR_INVALID
+    assert L.beam_dense_workspace_bytes(c, -1, ctypes.byref(n)) == B.ERR_INVALID
+    assert L.beam_dense_workspace_bytes(c, 0, ctypes.byref(n)) == B.OK and n.value == 0
+    assert L.beam_dense_mlp_forward(c, 0, *([None] * 9), 0, None) == B.OK
+    assert L.beam_dense_mlp_forward(None, 4, f, f, f, f, None, None, None, f, f, 1 << 40, None) == B.ERR_INVALID
+    assert L.beam_dense_mlp_forward(c, 4, None, f, f, f, None, None, None, f, f, 1 << 40, None) == B.ERR_INVALID
+    assert L.beam_dense_mlp_forward(c, 4, f, f, f, f, f, f, f, f, f, 1 << 40, None) == B.ERR_INVALID   # bf16 + scales
+    c8 = ctypes.byref(_dcfg(weight_type=B.W_FP8_E4M3))
+    assert L.beam_dense_mlp_forward(c8, 4, f, f, f, f, None, None, None, f, f, 1 << 40, None) == B.ERR_INVALID
+    need = bm.beam_dense_workspace_bytes(bm.DenseConfig(), 64)
+    assert L.beam_dense_mlp_forward(c, 64, f, f, f, f, None, None, None, f, f, need - 1, None) == B.ERR_WORKSPACE
+    assert L.beam_dense_mlp_forward(c, 64, f, f, f, f, None, None, None, f, None, need, None) == B.ERR_WORKSPACE
+
+
+def test_dense_workspace_holds_h_and_the_split_partials():
+    cfg = bm.DenseConfig()
+    small = bm.beam_dense_workspace_bytes(cfg, 64)
+    assert small >= 64 * cfg.inter * 2 + 2 * 64 * cfg.hidden * 4       # h plus at least two fp32 parts
+    assert bm.beam_dense_workspace_bytes(cfg, 8192) >= 8192 * cfg.inter * 2

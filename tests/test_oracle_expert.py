@@ -147,3 +147,32 @@ def test_combine_fixed_order():
             for k in range(K):
                 acc = np.float32(acc + np.float32(wts[t, k] * np.float32(yf[p2r[t * K + k], n])))
             assert out[t, n] == codecs.bf16_round_bits(np.array([acc], np.float32))[0]
+
+
+def test_dense_mlp_naive_loops_and_moe_reduction():
+    """The dense MLP oracle against exactly rounded loops, and against the MoE
+    layer with 32 identical experts (out = bf16(2.5 * dense), exact: y has 8
+    significant bits)."""
+    w, spec, src = _tiny_src(0)
+    x, wr, b = gen.router_inputs(w, 0)
+    e = 7
+    mats = [src.get(k, e) for k in ("gate", "up", "down")]
+    y = oracle.dense_mlp(x[:4], *mats)
+    X = codecs.bf16_to_f64(x[:4])
+    wg, wu, wd = (codecs.bf16_to_f64(m) for m in mats)
+    ref = np.zeros_like(y)
+    for r in range(X.shape[0]):
+        h = []
+        for i in range(spec.inter):
+            g = float(np.float32(math.fsum(X[r, hh] * wg[i, hh] for hh in range(spec.hidden))))
+            u = float(np.float32(math.fsum(X[r, hh] * wu[i, hh] for hh in range(spec.hidden))))
+            a = float(np.float32(g / (1.0 + math.exp(-g))))
+            h.append(float(codecs.bf16_to_f64(codecs.bf16_round_bits(np.float32(a * u)))))
+        for n in range(spec.hidden):
+            ref[r, n] = codecs.bf16_round_bits(np.array([math.fsum(h[i] * wd[n, i] for i in range(spec.inter))],
+                                                        np.float32))[0]
+    d = _ulps_bf16(y, ref)
+    assert d.max() <= 1 and (d == 0).mean() > 0.99
+    full = oracle.dense_mlp(x, *mats)
+    moe = oracle.forward(spec, x, wr, b, _identical_expert_weights(w, src, e))
+    _assert_rounds_to(moe["out"], 2.5 * codecs.bf16_to_f64(full))
