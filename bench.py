@@ -1,6 +1,7 @@
 """Benchmark of the Beam MoE block forward pass on one MI355X.
 
-    python bench.py [--workload decode|prefill|skew|fp8_decode|fp8_prefill] [--steps K] [--warmup W] [--block]
+    python bench.py [--workload decode|prefill|skew|fp8_decode|fp8_prefill|mxfp4_decode|mxfp4_prefill|
+                     spec_verify|dense_decode|dense_prefill] [--steps K] [--warmup W] [--block]
 
 A step is one beam_moe_forward call (router, selection, permutation, gate/up
 GEMM + SwiGLU, down GEMM, combine) over one batch of seeded synthetic inputs
@@ -36,7 +37,8 @@ STAGES = ["router_logits", "router_select", "permute", "gateup", "down", "combin
 BLOCK_STAGES = ["pre_norm", "router_logits", "router_select", "permute", "gateup", "down", "combine_norm_mix"]
 BLOCK_STEP, BLOCK_EPS = 23, 1e-6
 DEFAULTS = {"decode": (200, 20), "fp8_decode": (200, 20), "prefill": (30, 5), "skew": (40, 5), "fp8_prefill": (60, 5),
-            "spec_verify": (200, 20), "dense_decode": (200, 20), "dense_prefill": (30, 5)}
+            "mxfp4_decode": (200, 20), "mxfp4_prefill": (60, 5), "spec_verify": (200, 20), "dense_decode": (200, 20),
+            "dense_prefill": (30, 5)}
 DENSE_STAGES = ["setup", "gateup", "down"]
 
 
@@ -152,9 +154,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
     w = gen.workload(args.workload)
-    fp8 = w.weight == "fp8"
-    cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha,
-                    bm.W_FP8_E4M3 if fp8 else bm.W_BF16)
+    wtype = {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight]
+    cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha, wtype)
     log(f"[bench] {w.name}: T={w.T} H={w.hidden} I={w.inter} E={w.n_experts} weights={w.weight}")
     x_bits, wr, b = gen.router_inputs(w, args.seed)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -174,7 +175,7 @@ def main():
         sys.exit(2)
     stages = BLOCK_STAGES if args.block else (DENSE_STAGES if dense else STAGES)
     if dense:
-        dcfg = bm.DenseConfig(w.hidden, w.inter, bm.W_FP8_E4M3 if fp8 else bm.W_BF16)
+        dcfg = bm.DenseConfig(w.hidden, w.inter, wtype)
         Wd = {k: v[0] for k, v in W.items()}
         ws = torch.empty(max(1, bm.beam_dense_workspace_bytes(dcfg, w.T)), dtype=torch.uint8, device=dev)
     if args.block:
@@ -222,12 +223,15 @@ def main():
     load = np.bincount(ids_h.ravel(), minlength=w.n_experts)
     D = int((load > 0).sum())
     TK = w.T * w.top_k
-    wb = 1 if fp8 else 2
     H, I = w.hidden, w.inter
-    scale_b = 4 if fp8 else 0
-    gu_bytes = D * (2 * I * H * wb + 2 * I * scale_b) + w.T * H * 2 + TK * I * 2
-    dn_bytes = D * (H * I * wb + H * scale_b) + TK * I * 2 + TK * H * 2
-    layer_bytes = D * (3 * I * H * wb + (2 * I + H) * scale_b) + 2 * w.T * H * 2
+
+    def mat_bytes(rows, cols):
+        """Bytes of one [rows, cols] weight matrix with its scales."""
+        return {"bf16": 2 * rows * cols, "fp8": rows * cols + 4 * rows,
+                "mxfp4": rows * cols // 2 + rows * cols // 32}[w.weight]
+
+    gu_bytes = D * 2 * mat_bytes(I, H) + w.T * H * 2 + TK * I * 2
+    layer_bytes = D * (2 * mat_bytes(I, H) + mat_bytes(H, I)) + 2 * w.T * H * 2
     if not dense:
         layer_bytes += H * w.n_experts * 4 + w.n_experts * 4          # router weights and bias
     layer_flops = 6.0 * TK * H * I
@@ -236,7 +240,8 @@ def main():
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
     # the library's switch to the LDS-tiled kernels (the dense path streams up to 1024 tokens)
-    tiled = TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
+    tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
+             and w.weight != "mxfp4")
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
     gbps = gu_bytes / t_gu / 1e9
@@ -259,7 +264,8 @@ def main():
     res = {
         "metric": METRIC, "value": round(w.T / s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8-e4m3 weights, bf16 MFMA" if fp8 else "bf16",
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 MFMA",
+                                       "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 MFMA"}[w.weight],
         "data": "synthetic (seeded, random-init weights of the real layer shape)",
         "config": {"workload": (f"{w.name}: T={w.T}, dense SwiGLU MLP, hidden {H}, inter {I}" if dense else
                                 f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "

@@ -53,7 +53,14 @@ typedef enum {
   BEAM_MOE_ERR_HIP = -4           /* a HIP launch failed */
 } beam_moe_status;
 
-typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1 } beam_moe_wtype;
+/* Expert weight formats.  MXFP4 (OCP Microscaling: the MI355X analogue of the
+ * pages' NVFP4 checkpoint, overview page, section "Mixture of Experts"): each
+ * block of 32 consecutive inputs of an output row shares an E8M0 scale byte e
+ * (value 2^(e-127); codes 1..254), and each weight is an FP4 E2M1 code (values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte with the
+ * lower-indexed weight in the low nibble.  MXFP4 needs H and I to be multiples
+ * of 256 and runs on the weight-streaming kernels at every T. */
+typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1, BEAM_MOE_W_MXFP4 = 2 } beam_moe_wtype;
 
 typedef enum {
   BEAM_MOE_OP_ROUTE = 0,
@@ -66,8 +73,8 @@ typedef enum {
  * Beam's real shape: hidden 5120, inter 2560, 256 experts in 8 groups of 32,
  * 4 kept groups, top-8, alpha 2.5 (overview page, "Mixture of Experts"). */
 typedef struct {
-  int32_t hidden;       /* H: multiple of 128 */
-  int32_t inter;        /* I: multiple of 128 */
+  int32_t hidden;       /* H: multiple of 128 (256 for MXFP4) */
+  int32_t inter;        /* I: multiple of 128 (256 for MXFP4) */
   int32_t n_experts;    /* E: 1..256 */
   int32_t n_groups;     /* G: 1..64, E % G == 0 */
   int32_t topk_groups;  /* Gk: 1..G */
@@ -124,11 +131,13 @@ int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_
 
 /* The whole block: route, permute, grouped SwiGLU experts, weighted combine.
  *   x, w_router, b_router   as in beam_moe_route
- *   w_gate, w_up   [device] [E, I, H] bf16, or e4m3 bytes when weight_type is FP8
- *   w_down         [device] [E, H, I] bf16 or e4m3
- *   s_gate, s_up   [device] [E, I] fp32 per-output-channel scales (FP8 only, else NULL)
- *   s_down         [device] [E, H] fp32 (FP8 only, else NULL)
- *                  an FP8 weight's value is decode(q) * scale[e, out]
+ *   w_gate, w_up   [device] [E, I, H] bf16; e4m3 bytes (FP8); [E, I, H/2] packed E2M1 bytes (MXFP4)
+ *   w_down         [device] [E, H, I] bf16; e4m3 (FP8); [E, H, I/2] packed E2M1 (MXFP4)
+ *   s_gate, s_up   [device] FP8: [E, I] fp32 per-output-channel scales; MXFP4: [E, I, H/32]
+ *                  E8M0 bytes; BF16: NULL.  FP8 scales 4-byte aligned.
+ *   s_down         [device] FP8: [E, H] fp32; MXFP4: [E, H, I/32] E8M0 bytes; BF16: NULL
+ *                  an FP8 weight's value is decode(q) * scale[e, out]; an MXFP4
+ *                  weight's is e2m1(q) * 2^(scale[e, out, in/32] - 127)
  *   out            [device] [T, H] bf16 out
  *   topk_ids_out, topk_w_out  [device] optional [T, K] copies of the routing (may be NULL)
  *   workspace      [device] beam_moe_workspace_bytes(FORWARD) bytes
@@ -136,7 +145,7 @@ int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_
 int beam_moe_forward(const beam_moe_config* cfg, int32_t T,
                      const void* x, const float* w_router, const float* b_router,
                      const void* w_gate, const void* w_up, const void* w_down,
-                     const float* s_gate, const float* s_up, const float* s_down,
+                     const void* s_gate, const void* s_up, const void* s_down,
                      void* out, int32_t* topk_ids_out, float* topk_w_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
@@ -149,7 +158,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int32_t T,
 int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T,
                            const void* x, const float* w_router, const float* b_router,
                            const void* w_gate, const void* w_up, const void* w_down,
-                           const float* s_gate, const float* s_up, const float* s_down,
+                           const void* s_gate, const void* s_up, const void* s_down,
                            void* out, int32_t* topk_ids_out, float* topk_w_out,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
@@ -191,7 +200,7 @@ int beam_moe_block_forward(const beam_moe_config* cfg, int32_t T, int32_t step, 
                            const void* stream_in, const float* gamma_pre, const float* gamma_post,
                            const float* w_router, const float* b_router,
                            const void* w_gate, const void* w_up, const void* w_down,
-                           const float* s_gate, const float* s_up, const float* s_down,
+                           const void* s_gate, const void* s_up, const void* s_down,
                            void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
@@ -203,7 +212,7 @@ int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t 
                                  const void* stream_in, const float* gamma_pre, const float* gamma_post,
                                  const float* w_router, const float* b_router,
                                  const void* w_gate, const void* w_up, const void* w_down,
-                                 const float* s_gate, const float* s_up, const float* s_down,
+                                 const void* s_gate, const void* s_up, const void* s_down,
                                  void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* stage_events);
@@ -215,8 +224,8 @@ int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t 
  *   out[t,:] = bf16( W_down ( bf16( SiLU(W_gate x) * (W_up x) ) ) )
  * computed by the same grouped-GEMM kernels with one expert. */
 typedef struct {
-  int32_t hidden;       /* H: multiple of 128 */
-  int32_t inter;        /* I: multiple of 128 */
+  int32_t hidden;       /* H: multiple of 128 (256 for MXFP4) */
+  int32_t inter;        /* I: multiple of 128 (256 for MXFP4) */
   int32_t weight_type;  /* beam_moe_wtype */
 } beam_dense_config;
 
@@ -226,23 +235,38 @@ typedef struct {
 int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* bytes);
 
 /*   x              [device] [T, H] bf16
- *   w_gate, w_up   [device] [I, H] bf16, or e4m3 bytes with s_gate, s_up [I] fp32
- *   w_down         [device] [H, I] bf16, or e4m3 bytes with s_down [H] fp32
+ *   w_gate, w_up   [device] [I, H] bf16; e4m3 bytes with s_gate, s_up [I] fp32; or MXFP4
+ *                  [I, H/2] with s_gate, s_up [I, H/32] E8M0 bytes
+ *   w_down         [device] [H, I] bf16; e4m3 with s_down [H] fp32; or MXFP4 [H, I/2] with [H, I/32]
  *   out            [device] [T, H] bf16 out
  *   workspace      [device] beam_dense_workspace_bytes bytes
  * Deterministic: a split reduction adds its parts in a fixed order. */
 int beam_dense_mlp_forward(const beam_dense_config* cfg, int32_t T, const void* x,
                            const void* w_gate, const void* w_up, const void* w_down,
-                           const float* s_gate, const float* s_up, const float* s_down,
+                           const void* s_gate, const void* s_up, const void* s_down,
                            void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* beam_dense_mlp_forward with stage timestamps: stage_events is NULL or 4
  * hipEvent_t recorded on `stream`: 0 setup | 1 gate/up GEMM + SwiGLU | 2 down GEMM | 3 end. */
 int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const void* x,
                                  const void* w_gate, const void* w_up, const void* w_down,
-                                 const float* s_gate, const float* s_up, const float* s_down,
+                                 const void* s_gate, const void* s_up, const void* s_down,
                                  void* out, void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* stage_events);
+
+/* MXFP4 quantisation of bf16 rows (the OCP MX conversion rule): for each block
+ * of 32 consecutive values of a row, shared exponent = floor(log2(max |v|)) - 2
+ * (2 = E2M1's largest exponent), clamped to [-127, 127], scale byte = shared +
+ * 127 (0 for an all-zero block); each v / 2^shared is rounded to the nearest
+ * E2M1 value, ties to even mantissa, magnitudes past 6 saturating to 6; the
+ * sign bit is set for every v < 0 (so a small negative value becomes -0).
+ *   rows, cols  rows >= 0, cols >= 0 a multiple of 32; rows == 0 or cols == 0 is a no-op
+ *   w           [device] [rows, cols] bf16 (finite), 16-byte aligned
+ *   codes       [device] [rows, cols/2] packed E2M1 out (lower-indexed value in the low nibble), 16-byte aligned
+ *   scales      [device] [rows, cols/32] E8M0 bytes out
+ * Returns BEAM_MOE_ERR_INVALID for a bad size, a NULL or misaligned pointer.
+ * Integer and compare operations only: the result is exact and reproducible. */
+int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, void* scales, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,10 @@ Readings this oracle takes where the pages are silent:
     [out, in]; linear outputs are rounded to bf16 (the model dtype): h after the
     SwiGLU product, y after the down projection, and the combined output;
   * fp8 weights are OCP e4m3 codes with one fp32 scale per output channel; the
-    oracle dequantises the same bytes as fp32(decode(q) * scale).
+    oracle dequantises the same bytes as fp32(decode(q) * scale);
+  * MXFP4 weights (the MI355X analogue of the pages' NVFP4 checkpoint) are E2M1
+    codes, two per byte, with one E8M0 scale per 32 consecutive inputs of an
+    output row; their values e2m1(q) * 2^(e-127) are exact (oracle/codecs.py).
 
 Arithmetic: every dot product accumulates in float64 and is rounded once to
 float32 (f32) at the point the layer rounds; bf16 values enter exactly.
@@ -42,7 +45,7 @@ from typing import Callable
 
 import numpy as np
 
-from .codecs import bf16_round_bits, bf16_to_f64, e4m3_decode, f32
+from .codecs import bf16_round_bits, bf16_to_f64, e4m3_decode, f32, mxfp4_dequant
 
 GAP_GUARD = 1e-6
 
@@ -56,7 +59,7 @@ class LayerSpec:
     topk_groups: int
     top_k: int
     alpha: float
-    weight: str = "bf16"   # "bf16" | "fp8"
+    weight: str = "bf16"   # "bf16" | "fp8" | "mxfp4"
 
     @staticmethod
     def of(w) -> "LayerSpec":
@@ -181,9 +184,12 @@ def permute(ids: np.ndarray, n_experts: int):
 # --------------------------------------------------------- expert math -----
 
 def _dequant(spec: LayerSpec, mat) -> np.ndarray:
-    """Expert matrix as float64: bf16 bits exactly, or fp32(decode(q) * scale) for fp8."""
+    """Expert matrix as float64: bf16 bits exactly, fp32(decode(q) * scale) for fp8, e2m1 * 2^(e-127) for mxfp4."""
     if spec.weight == "bf16":
         return bf16_to_f64(mat)
+    if spec.weight == "mxfp4":
+        packed, e8 = mat
+        return mxfp4_dequant(packed, e8)
     q, scale = mat
     return f32(e4m3_decode(q).astype(np.float32).astype(np.float64)
                * np.asarray(scale, np.float64)[:, None]).astype(np.float64)
@@ -245,10 +251,11 @@ def dense_mlp(x_bits, wg, wu, wd, weight: str = "bf16") -> np.ndarray:
     expert's arithmetic and rounding points (expert_rows); no router, no combine.
 
     x_bits [T, H] bf16 bits; wg, wu [I, H], wd [H, I] as bf16 bits, or
-    (e4m3 codes, scales) pairs when weight == "fp8".  Returns bf16 bits [T, H].
+    (e4m3 codes, scales) pairs when weight == "fp8", or (packed E2M1 codes,
+    E8M0 scales) when weight == "mxfp4".  Returns bf16 bits [T, H].
     """
     x_bits = np.asarray(x_bits, np.uint16)
     H = x_bits.shape[1]
-    I = (wg[0] if weight == "fp8" else wg).shape[0]
+    I = (wg if weight == "bf16" else wg[0]).shape[0]
     spec = LayerSpec(H, I, 1, 1, 1, 1, 1.0, weight)
     return expert_rows(spec, bf16_to_f64(x_bits), wg, wu, wd)

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     OP_ROUTE,
     W_BF16,
     W_FP8_E4M3,
+    W_MXFP4,
     beam_dense_mlp_forward,
     beam_dense_workspace_bytes,
     beam_moe_block_forward,
@@ -27,5 +28,6 @@ from .binding import (  # noqa: F401
     beam_moe_rms_norm,
     beam_moe_route,
     beam_moe_workspace_bytes,
+    beam_mxfp4_quantize,
     status_string,
 )

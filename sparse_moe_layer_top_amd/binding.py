@@ -17,7 +17,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbeam_moe.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-W_BF16, W_FP8_E4M3 = 0, 1
+W_BF16, W_FP8_E4M3, W_MXFP4 = 0, 1, 2
 OP_ROUTE, OP_PERMUTE, OP_FORWARD, OP_BLOCK = 0, 1, 2, 3
 MAX_TOKENS = 262144
 MAX_NORM_HIDDEN = 8192
@@ -100,6 +100,8 @@ def _load():
     lib.beam_dense_mlp_forward.restype = ctypes.c_int
     lib.beam_dense_mlp_forward_timed.argtypes = [dcfgp, I32] + [P] * 9 + [SZ, P, P]
     lib.beam_dense_mlp_forward_timed.restype = ctypes.c_int
+    lib.beam_mxfp4_quantize.argtypes = [I32, I32, P, P, P, P]
+    lib.beam_mxfp4_quantize.restype = ctypes.c_int
     return lib
 
 
@@ -141,6 +143,28 @@ def _need(t: Optional[torch.Tensor], name: str, dtype, shape, device=None, optio
         raise ValueError(f"{name} must be a device tensor")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expert_weights(weight_type, lead, H, I, w_gate, w_up, w_down, s_gate, s_up, s_down, dev):
+    """Checks the gate/up [*lead, I, H] and down [*lead, H, I] weights and their scales for the weight type:
+    bf16 (no scales); e4m3 codes (uint8, same shape) with fp32 per-output-row scales [*lead, rows];
+    MXFP4 (uint8, two E2M1 codes a byte, low nibble first: [*lead, rows, cols/2]) with E8M0 scale bytes
+    [*lead, rows, cols/32]."""
+    lead = tuple(lead)
+    mats = ((w_gate, s_gate, "gate", I, H), (w_up, s_up, "up", I, H), (w_down, s_down, "down", H, I))
+    for w, sc, n, rows, cols in mats:
+        if weight_type == W_BF16:
+            _need(w, "w_" + n, torch.bfloat16, lead + (rows, cols), dev)
+        elif weight_type == W_FP8_E4M3:
+            _need(w, "w_" + n, torch.uint8, lead + (rows, cols), dev)
+            _need(sc, "s_" + n, torch.float32, lead + (rows,), dev)
+        elif weight_type == W_MXFP4:
+            _need(w, "w_" + n, torch.uint8, lead + (rows, cols // 2), dev)
+            _need(sc, "s_" + n, torch.uint8, lead + (rows, cols // 32), dev)
+        else:
+            raise ValueError(f"unknown weight_type {weight_type}")
+    if weight_type == W_BF16 and any(t is not None for t in (s_gate, s_up, s_down)):
+        raise ValueError("scales are only for fp8 and MXFP4 weights")
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -205,7 +229,8 @@ def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_rou
                      s_down: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                      topk_ids_out: Optional[torch.Tensor] = None, topk_w_out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stage_events=None) -> torch.Tensor:
-    """The whole MoE block.  Expert weights [E,I,H] / [E,H,I]: bf16, or uint8 e4m3 codes with fp32 scales.
+    """The whole MoE block.  Expert weights [E,I,H] / [E,H,I]: bf16, uint8 e4m3 codes with fp32 per-row
+    scales, or MXFP4 codes with E8M0 block scales (see _expert_weights).
 
     stage_events: None, or 7 recorded torch.cuda.Event(enable_timing=True)
     that the library records before each stage and after the last
@@ -215,16 +240,7 @@ def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_rou
     _need(x, "x", torch.bfloat16, (T, H))
     _need(w_router, "w_router", torch.float32, (H, E), dev)
     _need(b_router, "b_router", torch.float32, (E,), dev, optional=True)
-    wdt = torch.uint8 if cfg.weight_type == W_FP8_E4M3 else torch.bfloat16
-    _need(w_gate, "w_gate", wdt, (E, I, H), dev)
-    _need(w_up, "w_up", wdt, (E, I, H), dev)
-    _need(w_down, "w_down", wdt, (E, H, I), dev)
-    fp8 = cfg.weight_type == W_FP8_E4M3
-    _need(s_gate, "s_gate", torch.float32, (E, I), dev, optional=not fp8)
-    _need(s_up, "s_up", torch.float32, (E, I), dev, optional=not fp8)
-    _need(s_down, "s_down", torch.float32, (E, H), dev, optional=not fp8)
-    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
-        raise ValueError("scales are only for fp8 weights")
+    _expert_weights(cfg.weight_type, (E,), H, I, w_gate, w_up, w_down, s_gate, s_up, s_down, dev)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
@@ -278,16 +294,7 @@ def beam_moe_block_forward(cfg: Config, step: int, eps: float, stream_in: torch.
     _need(gamma_post, "gamma_post", torch.float32, (H,), dev)
     _need(w_router, "w_router", torch.float32, (H, E), dev)
     _need(b_router, "b_router", torch.float32, (E,), dev, optional=True)
-    fp8 = cfg.weight_type == W_FP8_E4M3
-    wdt = torch.uint8 if fp8 else torch.bfloat16
-    _need(w_gate, "w_gate", wdt, (E, I, H), dev)
-    _need(w_up, "w_up", wdt, (E, I, H), dev)
-    _need(w_down, "w_down", wdt, (E, H, I), dev)
-    _need(s_gate, "s_gate", torch.float32, (E, I), dev, optional=not fp8)
-    _need(s_up, "s_up", torch.float32, (E, I), dev, optional=not fp8)
-    _need(s_down, "s_down", torch.float32, (E, H), dev, optional=not fp8)
-    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
-        raise ValueError("scales are only for fp8 weights")
+    _expert_weights(cfg.weight_type, (E,), H, I, w_gate, w_up, w_down, s_gate, s_up, s_down, dev)
     if stream_out is None:
         stream_out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     _need(stream_out, "stream_out", torch.bfloat16, (T, H), dev)
@@ -320,21 +327,12 @@ def beam_dense_mlp_forward(cfg: DenseConfig, x: torch.Tensor, w_gate: torch.Tens
                            s_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                            stage_events=None) -> torch.Tensor:
-    """Dense SwiGLU MLP: out = bf16(W_down bf16(SiLU(W_gate x) * (W_up x))).  Weights [I,H] / [H,I]: bf16, or
-    uint8 e4m3 codes with fp32 per-output scales.  stage_events: None or 4 recorded torch.cuda.Event objects."""
+    """Dense SwiGLU MLP: out = bf16(W_down bf16(SiLU(W_gate x) * (W_up x))).  Weights [I,H] / [H,I]: bf16,
+    uint8 e4m3 codes with fp32 per-output scales, or MXFP4 (see _expert_weights).  stage_events: None or 4 recorded torch.cuda.Event objects."""
     T, dev = x.shape[0], x.device
     H, I = cfg.hidden, cfg.inter
-    fp8 = cfg.weight_type == W_FP8_E4M3
-    wdt = torch.uint8 if fp8 else torch.bfloat16
     _need(x, "x", torch.bfloat16, (T, H))
-    _need(w_gate, "w_gate", wdt, (I, H), dev)
-    _need(w_up, "w_up", wdt, (I, H), dev)
-    _need(w_down, "w_down", wdt, (H, I), dev)
-    _need(s_gate, "s_gate", torch.float32, (I,), dev, optional=not fp8)
-    _need(s_up, "s_up", torch.float32, (I,), dev, optional=not fp8)
-    _need(s_down, "s_down", torch.float32, (H,), dev, optional=not fp8)
-    if not fp8 and any(t is not None for t in (s_gate, s_up, s_down)):
-        raise ValueError("scales are only for fp8 weights")
+    _expert_weights(cfg.weight_type, (), H, I, w_gate, w_up, w_down, s_gate, s_up, s_down, dev)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
@@ -353,3 +351,27 @@ def beam_dense_mlp_forward(cfg: DenseConfig, x: torch.Tensor, w_gate: torch.Tens
         arr = (ctypes.c_void_p * 4)(*[ev.cuda_event for ev in stage_events])
         _check("beam_dense_mlp_forward_timed", LIB.beam_dense_mlp_forward_timed(*args, arr))
     return out
+
+
+def beam_mxfp4_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                        scales: Optional[torch.Tensor] = None):
+    """MXFP4 encoding of bf16 rows w [..., cols] (cols % 32 == 0): returns (codes [..., cols/2] uint8,
+    scales [..., cols/32] uint8), the layout the MXFP4 weight type reads."""
+    if w.dim() < 1:
+        raise ValueError("w must have at least one dimension")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    lead = tuple(w.shape[:-1])
+    dev = w.device
+    _need(w, "w", torch.bfloat16, tuple(w.shape))
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    if codes is None:
+        codes = torch.empty(lead + (cols // 2,), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(lead + (cols // 32,), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, lead + (cols // 2,), dev)
+    _need(scales, "scales", torch.uint8, lead + (cols // 32,), dev)
+    _check("beam_mxfp4_quantize", LIB.beam_mxfp4_quantize(rows, cols, _ptr(w), _ptr(codes), _ptr(scales),
+                                                          _stream(dev)))
+    return codes, scales

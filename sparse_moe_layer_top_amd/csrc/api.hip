@@ -28,16 +28,20 @@ int check_config(const beam_moe_config* c) {
   if (c->topk_groups > c->n_groups) return BEAM_MOE_ERR_INVALID;
   if ((long)c->top_k > (long)c->topk_groups * (c->n_experts / c->n_groups)) return BEAM_MOE_ERR_INVALID;
   if (!isfinite(c->routed_scale)) return BEAM_MOE_ERR_INVALID;
-  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3) return BEAM_MOE_ERR_INVALID;
+  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3 && c->weight_type != BEAM_MOE_W_MXFP4)
+    return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->n_experts > beam::kMaxExperts || c->n_groups > 64 || c->top_k > beam::kMaxTopK)
     return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;
 }
 
 Shape shape_of(const beam_moe_config* c) {
-  return Shape{c->hidden, c->inter, c->n_experts, c->n_groups, c->topk_groups, c->top_k, c->routed_scale,
-               c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
+  Shape s{c->hidden, c->inter, c->n_experts, c->n_groups, c->topk_groups, c->top_k, c->routed_scale,
+          c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
+  s.mx = c->weight_type == BEAM_MOE_W_MXFP4;
+  return s;
 }
 
 // Router K-split: kc = H/ks is a multiple of 32, between 128 and 1280 where
@@ -105,16 +109,17 @@ P* at(void* ws, size_t off) {
 
 // Checks shared by forward and block (config already checked, T > 0).
 int check_forward_args(const beam_moe_config* cfg, const void* x, const float* w_router, const float* b_router,
-                       const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
-                       const float* s_up, const float* s_down, const void* out, const int32_t* topk_ids_out,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                       const void* s_up, const void* s_down, const void* out, const int32_t* topk_ids_out,
                        const float* topk_w_out) {
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
-  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
-  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
+  const bool scaled = cfg->weight_type != BEAM_MOE_W_BF16;   // fp8 per-channel or MXFP4 block scales
+  if (scaled != (s_gate != nullptr) || scaled != (s_up != nullptr) || scaled != (s_down != nullptr))
     return BEAM_MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
       !aligned16(out) || (b_router && !aligned4(b_router)) || (topk_ids_out && !aligned4(topk_ids_out)) ||
-      (topk_w_out && !aligned4(topk_w_out)) || (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+      (topk_w_out && !aligned4(topk_w_out)) ||
+      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
     return BEAM_MOE_ERR_INVALID;
   return BEAM_MOE_OK;
 }
@@ -130,8 +135,8 @@ struct BlockEpilogue {
 
 // Router .. combine on x; `ev` (optional) gets one event before each stage and one after the last.
 int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, const float* w_router,
-                const float* b_router, const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
-                const float* s_up, const float* s_down, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
+                const float* b_router, const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                const void* s_up, const void* s_down, uint16_t* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* workspace, hipStream_t hs, void* const* ev, const BlockEpilogue* blk) {
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
   float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
@@ -173,14 +178,17 @@ int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, cons
 
 int check_dense_config(const beam_dense_config* c) {
   if (!c || c->hidden <= 0 || c->inter <= 0) return BEAM_MOE_ERR_INVALID;
-  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3) return BEAM_MOE_ERR_INVALID;
+  if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3 && c->weight_type != BEAM_MOE_W_MXFP4)
+    return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;
 }
 
 Shape dense_shape(const beam_dense_config* c) {
   Shape s{c->hidden, c->inter, 1, 1, 1, 1, 1.0f, c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
   s.dense = 1;
+  s.mx = c->weight_type == BEAM_MOE_W_MXFP4;
   return s;
 }
 
@@ -281,7 +289,7 @@ int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_
 
 int beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
                      const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
-                     const float* s_gate, const float* s_up, const float* s_down, void* out, int32_t* topk_ids_out,
+                     const void* s_gate, const void* s_up, const void* s_down, void* out, int32_t* topk_ids_out,
                      float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
   return beam_moe_forward_timed(cfg, T, x, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, out,
                                 topk_ids_out, topk_w_out, workspace, workspace_bytes, stream, nullptr);
@@ -289,7 +297,7 @@ int beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x, const
 
 int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
                            const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
-                           const float* s_gate, const float* s_up, const float* s_down, void* out,
+                           const void* s_gate, const void* s_up, const void* s_down, void* out,
                            int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* stage_events) {
   int st = check_config(cfg);
@@ -322,7 +330,7 @@ int beam_moe_rms_norm(int32_t T, int32_t hidden, const void* x, const float* gam
 int beam_moe_block_forward(const beam_moe_config* cfg, int32_t T, int32_t step, float eps, const void* stream_in,
                            const float* gamma_pre, const float* gamma_post, const float* w_router,
                            const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
-                           const float* s_gate, const float* s_up, const float* s_down, void* stream_out,
+                           const void* s_gate, const void* s_up, const void* s_down, void* stream_out,
                            void* moe_out, int32_t* topk_ids_out, float* topk_w_out, void* workspace,
                            size_t workspace_bytes, void* stream) {
   return beam_moe_block_forward_timed(cfg, T, step, eps, stream_in, gamma_pre, gamma_post, w_router, b_router, w_gate,
@@ -333,7 +341,7 @@ int beam_moe_block_forward(const beam_moe_config* cfg, int32_t T, int32_t step, 
 int beam_moe_block_forward_timed(const beam_moe_config* cfg, int32_t T, int32_t step, float eps,
                                  const void* stream_in, const float* gamma_pre, const float* gamma_post,
                                  const float* w_router, const float* b_router, const void* w_gate, const void* w_up,
-                                 const void* w_down, const float* s_gate, const float* s_up, const float* s_down,
+                                 const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
                                  void* stream_out, void* moe_out, int32_t* topk_ids_out, float* topk_w_out,
                                  void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
   int st = check_config(cfg);
@@ -372,26 +380,26 @@ int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* 
 }
 
 int beam_dense_mlp_forward(const beam_dense_config* cfg, int32_t T, const void* x, const void* w_gate,
-                           const void* w_up, const void* w_down, const float* s_gate, const float* s_up,
-                           const float* s_down, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                           const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                           const void* s_down, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return beam_dense_mlp_forward_timed(cfg, T, x, w_gate, w_up, w_down, s_gate, s_up, s_down, out, workspace,
                                       workspace_bytes, stream, nullptr);
 }
 
 int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const void* x, const void* w_gate,
-                                 const void* w_up, const void* w_down, const float* s_gate, const float* s_up,
-                                 const float* s_down, void* out, void* workspace, size_t workspace_bytes,
+                                 const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                                 const void* s_down, void* out, void* workspace, size_t workspace_bytes,
                                  void* stream, void* const* stage_events) {
   int st = check_dense_config(cfg);
   if (st != BEAM_MOE_OK) return st;
   if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
   if (T == 0) return BEAM_MOE_OK;
   if (!x || !w_gate || !w_up || !w_down || !out) return BEAM_MOE_ERR_INVALID;
-  const bool fp8 = cfg->weight_type == BEAM_MOE_W_FP8_E4M3;
-  if (fp8 != (s_gate != nullptr) || fp8 != (s_up != nullptr) || fp8 != (s_down != nullptr))
+  const bool scaled = cfg->weight_type != BEAM_MOE_W_BF16;   // fp8 per-channel or MXFP4 block scales
+  if (scaled != (s_gate != nullptr) || scaled != (s_up != nullptr) || scaled != (s_down != nullptr))
     return BEAM_MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) ||
-      (s_gate && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
     return BEAM_MOE_ERR_INVALID;
   const Shape s = dense_shape(cfg);
   const DenseLayout L = dense_layout(s, T);
@@ -415,6 +423,15 @@ int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const 
   BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, L.kparts, part,
                                  static_cast<uint16_t*>(out), hs));
   BEAM_TRY_HIP(mark(3));
+  return BEAM_MOE_OK;
+}
+
+int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, void* scales, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return BEAM_MOE_ERR_INVALID;
+  if (rows == 0 || cols == 0) return BEAM_MOE_OK;
+  if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return BEAM_MOE_ERR_INVALID;
+  BEAM_TRY_HIP(beam::launch_mxfp4_quantize(rows, cols, static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
+                                           static_cast<uint8_t*>(scales), static_cast<hipStream_t>(stream)));
   return BEAM_MOE_OK;
 }
 

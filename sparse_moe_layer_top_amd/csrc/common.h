@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -25,6 +27,7 @@ struct Shape {
   float alpha;
   int fp8;
   int dense = 0;   // one expert holding every token (a dense SwiGLU MLP): no router, no combine
+  int mx = 0;      // MXFP4 weights (E2M1 codes + E8M0 block scales); fp8 is 0 then
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -49,6 +52,18 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 q) {
   return r;
 }
 
+// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times a
+// power-of-two block scale -> 8 bf16 values, exact (v_cvt_scalef32_pk_bf16_fp4;
+// results assembled through 32-bit casts).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t q, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ---- workspace carve-up (host) ----
@@ -68,16 +83,18 @@ hipError_t launch_permute(const Shape& s, int T, const int32_t* ids, int nchunks
                           int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
                           int tile_rows, int32_t* tiles, int32_t* ntiles, hipStream_t stream);
 hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
-                         const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                         const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                          hipStream_t stream);
-hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
+hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part,
                        uint16_t* y, hipStream_t stream);
 hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float* w,
                           const int32_t* pair_to_row, uint16_t* out, hipStream_t stream);
 int down_kparts(const Shape& s, int T);
+hipError_t launch_mxfp4_quantize(int rows, int cols, const uint16_t* w, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
 hipError_t launch_dense_setup(int T, int tile_rows, int32_t* offsets, int32_t* sorted_pairs, int32_t* tiles,
                               int32_t* ntiles, hipStream_t stream);
 hipError_t launch_rms_norm(int T, int H, float eps, const uint16_t* in, const float* gamma, uint16_t* out,

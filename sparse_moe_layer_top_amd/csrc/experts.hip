@@ -16,28 +16,51 @@
 //
 // FP8 weights (OCP e4m3) are converted exactly to bf16 in registers; the
 // per-output-channel scale multiplies the fp32 accumulator in the epilogue.
+// MXFP4 weights (E2M1, two per byte, one E8M0 scale per 32 inputs) are
+// converted with their block scale to bf16 in registers (exact: a power of
+// two times a 2-bit-significand value); one 16-byte load holds 32 values, a
+// whole scale block.
 #include <type_traits>
 
 #include "common.h"
 
 namespace beam {
 
-template <bool FP8>
+enum { kWBF16 = 0, kWFP8 = 1, kWMX = 2 };
+
+template <int WT>
 struct WFrag;   // one lane's 16-byte weight load per k-step and its conversion to MFMA B-fragments
 template <>
-struct WFrag<false> {
+struct WFrag<kWBF16> {
   using E = uint16_t;
-  static constexpr int SK = 32;   // k per step: one 16x16x32 MFMA
-  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int) { return __builtin_bit_cast(bf16x8, v); }
+  static constexpr int SK = 32;     // k per step: one 16x16x32 MFMA
+  static constexpr int SE = 32;     // weight elements (of type E) per row per step
+  static constexpr bool kBlockScale = false;
+  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int, float) { return __builtin_bit_cast(bf16x8, v); }
 };
 template <>
-struct WFrag<true> {
+struct WFrag<kWFP8> {
   using E = uint8_t;
-  static constexpr int SK = 64;   // k per step: 16 e4m3 bytes feed two MFMAs
-  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int a) {
+  static constexpr int SK = 64;     // 16 e4m3 bytes feed two MFMAs
+  static constexpr int SE = 64;
+  static constexpr bool kBlockScale = false;
+  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int a, float) {
     return e4m3x8_to_bf16x8(a == 0 ? u32x2{v[0], v[1]} : u32x2{v[2], v[3]});
   }
 };
+template <>
+struct WFrag<kWMX> {
+  using E = uint8_t;
+  static constexpr int SK = 128;    // 16 bytes = 32 E2M1 values per lane feed four MFMAs
+  static constexpr int SE = 64;     // bytes per row per step
+  static constexpr bool kBlockScale = true;
+  static __device__ __forceinline__ bf16x8 frag(u32x4 v, int a, float scale) { return e2m1x8_to_bf16x8(v[a], scale); }
+};
+
+// E8M0 block scale byte -> float 2^(e-127) (codes 1..254; 0 gives 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -56,12 +79,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // fences keep the compiler from reordering the bursts.  nsteps must be a
 // multiple of 2*D (the caller picks D so): a remainder loop after the
 // pipelined one makes the compiler schedule the whole loop worse.
-template <bool FP8, int MT, int NB, int D>
-__device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<FP8>::E* const (&wrow)[NB],
-                                         const uint16_t* const (&arow)[MT], f32x4 (&acc)[MT][NB]) {
-  using W = WFrag<FP8>;
-  constexpr int SK = W::SK, NA = SK / 32;
+template <int WT, int MT, int NB, int D>
+__device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<WT>::E* const (&wrow)[NB],
+                                         const uint8_t* const (&srow)[NB], const uint16_t* const (&arow)[MT],
+                                         f32x4 (&acc)[MT][NB]) {
+  using W = WFrag<WT>;
+  constexpr int SK = W::SK, SE = W::SE, NA = SK / 32;
   u32x4 wb[2][D][NB];
+  uint32_t sb[2][D][W::kBlockScale ? NB : 1];
   bf16x8 ab[2][D][MT][NA];
   const int nwin = nsteps / D;
   auto load = [&](int buf, int w) {
@@ -69,7 +94,10 @@ __device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<FP8>::
 #pragma unroll
     for (int j = 0; j < D; ++j) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SK);
+      for (int nb = 0; nb < NB; ++nb) {
+        wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SE);
+        if constexpr (W::kBlockScale) sb[buf][j][nb] = srow[nb][(base + j) * (SK / 32)];
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -81,13 +109,15 @@ __device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<FP8>::
 #pragma unroll
     for (int j = 0; j < D; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const float sc = W::kBlockScale ? e8m0_to_f32(sb[buf][j][W::kBlockScale ? nb : 0]) : 1.f;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-          const bf16x8 b = W::frag(wb[buf][j][nb], a);
+          const bf16x8 b = W::frag(wb[buf][j][nb], a, sc);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt][nb] = mfma16(ab[buf][j][mt][a], b, acc[mt][nb]);
         }
+      }
   };
   load(0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -104,22 +134,25 @@ __device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<FP8>::
 }
 
 // Burst depth cap by register budget: 2*D*(NB + MT*SK/32) 16-byte registers per lane.
-template <bool FP8, int MT>
-struct MaxDepth { static constexpr int value = (MT == 1) ? 4 : (MT == 2 ? (FP8 ? 2 : 4) : (FP8 ? 1 : 2)); };
+template <int WT, int MT>
+struct MaxDepth {
+  static constexpr int value = WT == kWMX ? (MT == 1 ? 2 : 1)
+                                          : (MT == 1 ? 4 : (MT == 2 ? (WT == kWFP8 ? 2 : 4) : (WT == kWFP8 ? 1 : 2)));
+};
 
 // gate/up: grid (max_tiles, I/64), 4 waves; wave w owns columns [64*by + 16*w, +16) of gate and up.
 // Rows past the tile's end read a valid row (the tile's first) and their
 // outputs are discarded: an MFMA output row depends only on its own A row.
-template <bool FP8, int MT, int D>
+template <int WT, int MT, int D>
 __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K, const uint16_t* __restrict__ x,
                                                             const void* __restrict__ wg, const void* __restrict__ wu,
-                                                            const float* __restrict__ sg, const float* __restrict__ su,
+                                                            const void* __restrict__ sg, const void* __restrict__ su,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted_pairs,
                                                             const int32_t* __restrict__ tiles,
                                                             const int32_t* __restrict__ ntiles,
                                                             uint16_t* __restrict__ h) {
-  using W = WFrag<FP8>;
+  using W = WFrag<WT>;
   const int tile = blockIdx.x;
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
@@ -128,27 +161,34 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int l16 = lane % 16, q = lane / 16;
   const int col = blockIdx.y * 64 + wave * 16 + l16;
-  const int qk = q * (W::SK / 4);
+  const int qa = q * (W::SK / 4), qw = q * (W::SE / 4);   // lane quad offsets: activations (k), weights (E units)
 
   const uint16_t* xr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
     const int tok = sorted_pairs[lo + r0 + (r < rows ? r : 0)] / K;
-    xr[mt] = x + (size_t)tok * H + qk;
+    xr[mt] = x + (size_t)tok * H + qa;
   }
   using WE = typename W::E;
-  const size_t wrow = ((size_t)e * I + col) * H + qk;
+  const size_t row = (size_t)e * I + col;
+  const size_t wrow = row * ((size_t)H * W::SE / W::SK) + qw;
   const WE* const wr[2] = {static_cast<const WE*>(wg) + wrow, static_cast<const WE*>(wu) + wrow};
+  const uint8_t* sr[2] = {nullptr, nullptr};
+  if constexpr (W::kBlockScale) {
+    const size_t srow = row * (H / 32) + q;
+    sr[0] = static_cast<const uint8_t*>(sg) + srow;
+    sr[1] = static_cast<const uint8_t*>(su) + srow;
+  }
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<FP8, MT, 2, D>(H / W::SK, wr, xr, acc);
+  stream_k<WT, MT, 2, D>(H / W::SK, wr, sr, xr, acc);
 
   float scg = 1.f, scu = 1.f;
-  if constexpr (FP8) {
-    scg = sg[(size_t)e * I + col];
-    scu = su[(size_t)e * I + col];
+  if constexpr (WT == kWFP8) {
+    scg = static_cast<const float*>(sg)[row];
+    scu = static_cast<const float*>(su)[row];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -163,19 +203,18 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   }
 }
 
-// down: grid (max_tiles, H/128), 4 waves; wave w owns columns [128*by + 32*w, +32) as two 16-col blocks.
 // With kparts > 1 (grid z), part z covers reduction steps [z*n, (z+1)*n) and
 // writes its raw fp32 sums to part[z][row][col]; splitk_reduce_kernel adds the
 // parts in z order.  Used when one expert's rows are too few to fill the chip.
-template <bool FP8, int MT, int D>
+template <int WT, int MT, int D>
 __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const uint16_t* __restrict__ hbuf,
-                                                          const void* __restrict__ wd, const float* __restrict__ sd,
+                                                          const void* __restrict__ wd, const void* __restrict__ sd,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
                                                           uint16_t* __restrict__ y, int kparts, int nrows,
                                                           float* __restrict__ part) {
-  using W = WFrag<FP8>;
+  using W = WFrag<WT>;
   const int tile = blockIdx.x;
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
@@ -185,27 +224,34 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
   const int l16 = lane % 16, q = lane / 16;
   const int c0 = blockIdx.y * 128 + wave * 32;
   if (c0 >= H) return;   // wave-uniform; H % 32 == 0 so both 16-column blocks are in range
-  const int qk = q * (W::SK / 4);
+  const int qa = q * (W::SK / 4), qw = q * (W::SE / 4);
 
   const uint16_t* hr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
-    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + qk;
+    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + qa;
   }
   using WE = typename W::E;
-  const size_t w0 = ((size_t)e * H + c0 + l16) * I + qk;
-  const WE* const wr[2] = {static_cast<const WE*>(wd) + w0, static_cast<const WE*>(wd) + w0 + (size_t)16 * I};
+  const size_t IE = (size_t)I * W::SE / W::SK;          // a weight row in E units
+  const size_t row0 = (size_t)e * H + c0 + l16;
+  const WE* wr[2] = {static_cast<const WE*>(wd) + row0 * IE + qw, static_cast<const WE*>(wd) + (row0 + 16) * IE + qw};
+  const uint8_t* sr[2] = {nullptr, nullptr};
+  if constexpr (W::kBlockScale) {
+    sr[0] = static_cast<const uint8_t*>(sd) + row0 * (I / 32) + q;
+    sr[1] = static_cast<const uint8_t*>(sd) + (row0 + 16) * (I / 32) + q;
+  }
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = I / W::SK / kparts;
   if (kparts > 1) {
-    const size_t koff = (size_t)blockIdx.z * nsteps * W::SK;
+    const size_t zs = (size_t)blockIdx.z * nsteps;       // first step of this part
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) hr[mt] += koff;
-    const WE* const wk[2] = {wr[0] + koff, wr[1] + koff};
-    stream_k<FP8, MT, 2, D>(nsteps, wk, hr, acc);
+    for (int mt = 0; mt < MT; ++mt) hr[mt] += zs * W::SK;
+    const WE* const wk[2] = {wr[0] + zs * W::SE, wr[1] + zs * W::SE};
+    const uint8_t* const sk[2] = {sr[0] ? sr[0] + zs * (W::SK / 32) : nullptr, sr[1] ? sr[1] + zs * (W::SK / 32) : nullptr};
+    stream_k<WT, MT, 2, D>(nsteps, wk, sk, hr, acc);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -219,12 +265,14 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
       }
     return;
   }
-  stream_k<FP8, MT, 2, D>(nsteps, wr, hr, acc);
+  const WE* const wk[2] = {wr[0], wr[1]};
+  const uint8_t* const sk[2] = {sr[0], sr[1]};
+  stream_k<WT, MT, 2, D>(nsteps, wk, sk, hr, acc);
 
   float s0 = 1.f, s1 = 1.f;
-  if constexpr (FP8) {
-    s0 = sd[(size_t)e * H + c0 + l16];
-    s1 = sd[(size_t)e * H + c0 + 16 + l16];
+  if constexpr (WT == kWFP8) {
+    s0 = static_cast<const float*>(sd)[row0];
+    s1 = static_cast<const float*>(sd)[row0 + 16];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -255,27 +303,27 @@ static int pick_depth(int nsteps, int cap) {
   return 1;
 }
 
-template <bool FP8, int MT, int D>
-static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
-                                const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+template <int WT, int MT, int D>
+static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const void* sg,
+                                const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                                 const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_stream_kernel<FP8, MT, D>), dim3(max_tiles, s.I / 64), dim3(256), 0, stream, s.H, s.I,
+  hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, D>), dim3(max_tiles, s.I / 64), dim3(256), 0, stream, s.H, s.I,
                      s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h);
   return hipGetLastError();
 }
 
-template <bool FP8, int MT, int D>
-static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
+template <int WT, int MT, int D>
+static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd, const void* sd,
                               const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                               uint16_t* y, int kparts, int nrows, float* part, hipStream_t stream) {
-  hipLaunchKernelGGL((down_stream_kernel<FP8, MT, D>), dim3(max_tiles, (s.H + 127) / 128, kparts), dim3(256), 0,
+  hipLaunchKernelGGL((down_stream_kernel<WT, MT, D>), dim3(max_tiles, (s.H + 127) / 128, kparts), dim3(256), 0,
                      stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part);
   return hipGetLastError();
 }
 
 // y[row][col] = bf16( (part[0] + part[1] + ... + part[kparts-1]) * scale[col] ), parts added in order.
-// One expert (the dense path): the fp8 scale of output column col is sd[col].
+// One expert (the dense path): the fp8 scale of output column col is sd[col] (NULL: no scale).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(int nrows, int H, int kparts, const float* __restrict__ part,
                                                             const float* __restrict__ sd, uint16_t* __restrict__ y) {
   const size_t n = (size_t)nrows * H;
@@ -298,27 +346,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int nrows, int H, in
   }
 }
 
-// Reduction parts for the dense path's down GEMM: the fewest parts (a divisor
-// of the step count / 8, so each part keeps the deepest burst schedule) that
-// give about 1024 workgroups; 1 when the row tiles alone do.
+static int weight_type_of(const Shape& s) { return s.mx ? kWMX : (s.fp8 ? kWFP8 : kWBF16); }
+
+static int steps_per_k(const Shape& s, int K) {
+  return K / (s.mx ? WFrag<kWMX>::SK : (s.fp8 ? WFrag<kWFP8>::SK : WFrag<kWBF16>::SK));
+}
+
+// Reduction parts for the dense path's down GEMM: the fewest parts giving about
+// 1024 workgroups, each part an even number of steps (a multiple of 8 where the
+// step count allows, keeping the deepest burst schedule); 1 when the row tiles
+// alone fill the GPU.
 int down_kparts(const Shape& s, int T) {
   if (!s.dense || use_tiled(s, T)) return 1;
   const int bm = expert_tile_rows(s, T);
   const long wgs = (long)((T + bm - 1) / bm) * ((s.H + 127) / 128);
-  const int units = s.I / WFrag<false>::SK / 8 / (s.fp8 ? 2 : 1);   // steps / 8 for the weight type
+  const int steps = steps_per_k(s, s.I);
+  const int grain = steps % 8 == 0 ? 8 : 2;
   int best = 1;
-  for (int k = 1; k <= 32 && k <= units; ++k) {
-    if (units % k) continue;
+  for (int k = 1; k <= 32 && k * grain <= steps; ++k) {
+    if (steps % (k * grain)) continue;
     best = k;
     if (wgs * k >= 1024) break;
   }
   return best;
 }
 
-// Dispatch on (fp8, row-tile count, depth).
-template <bool FP8, int MT, typename F>
+// Dispatch on (weight type, row-tile count, depth).
+template <int WT, int MT, typename F>
 static hipError_t with_depth(int nsteps, F&& f) {
-  constexpr int cap = MaxDepth<FP8, MT>::value;
+  constexpr int cap = MaxDepth<WT, MT>::value;
   switch (pick_depth(nsteps, cap)) {
     case 4: return f(std::integral_constant<int, (cap >= 4 ? 4 : 1)>{});
     case 2: return f(std::integral_constant<int, (cap >= 2 ? 2 : 1)>{});
@@ -326,56 +382,56 @@ static hipError_t with_depth(int nsteps, F&& f) {
   }
 }
 
-hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
-                         const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
-                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
-                         hipStream_t stream) {
-  if (use_tiled(s, T))
-    return launch_gateup_tiled(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
-  const int bm = expert_tile_rows(s, T);
-  auto go = [&](auto fp8, auto mt) {
-    constexpr bool F = decltype(fp8)::value;
-    constexpr int M = decltype(mt)::value;
-    return with_depth<F, M>(s.H / WFrag<F>::SK, [&](auto d) {
-      return gateup_launch<F, M, decltype(d)::value>(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles,
-                                                     max_tiles, h, stream);
-    });
-  };
-  using B = std::bool_constant<false>;
-  using F8 = std::bool_constant<true>;
+template <typename G>
+static hipError_t dispatch_wt_mt(const Shape& s, int bm, G&& go) {
   using M1 = std::integral_constant<int, 1>;
   using M2 = std::integral_constant<int, 2>;
   using M4 = std::integral_constant<int, 4>;
-  if (s.fp8) return bm == 16 ? go(F8{}, M1{}) : bm == 32 ? go(F8{}, M2{}) : go(F8{}, M4{});
-  return bm == 16 ? go(B{}, M1{}) : bm == 32 ? go(B{}, M2{}) : go(B{}, M4{});
+  auto by_mt = [&](auto wt) { return bm == 16 ? go(wt, M1{}) : bm == 32 ? go(wt, M2{}) : go(wt, M4{}); };
+  switch (weight_type_of(s)) {
+    case kWMX: return by_mt(std::integral_constant<int, kWMX>{});
+    case kWFP8: return by_mt(std::integral_constant<int, kWFP8>{});
+    default: return by_mt(std::integral_constant<int, kWBF16>{});
+  }
 }
 
-hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
+hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
+                         const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                         hipStream_t stream) {
+  if (use_tiled(s, T))
+    return launch_gateup_tiled(s, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
+                               sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+  return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
+    constexpr int WT = decltype(wt)::value;
+    constexpr int M = decltype(mt)::value;
+    return with_depth<WT, M>(s.H / WFrag<WT>::SK, [&](auto d) {
+      return gateup_launch<WT, M, decltype(d)::value>(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles,
+                                                      max_tiles, h, stream);
+    });
+  });
+}
+
+hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part, uint16_t* y, hipStream_t stream) {
-  if (use_tiled(s, T)) return launch_down_tiled(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
-  const int bm = expert_tile_rows(s, T);
+  if (use_tiled(s, T))
+    return launch_down_tiled(s, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles, y, stream);
   const int nrows = T * s.K;
-  auto go = [&](auto fp8, auto mt) {
-    constexpr bool F = decltype(fp8)::value;
+  return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
+    constexpr int WT = decltype(wt)::value;
     constexpr int M = decltype(mt)::value;
-    hipError_t err = with_depth<F, M>(s.I / WFrag<F>::SK / kparts, [&](auto d) {
-      return down_launch<F, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, kparts, nrows,
-                                                   part, stream);
+    hipError_t err = with_depth<WT, M>(s.I / WFrag<WT>::SK / kparts, [&](auto d) {
+      return down_launch<WT, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, kparts, nrows,
+                                                    part, stream);
     });
     if (err != hipSuccess || kparts == 1) return err;
     const size_t n4 = (size_t)nrows * s.H / 4;
     const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, nrows, s.H, kparts, part, sd, y);
+    const float* fsd = WT == kWFP8 ? static_cast<const float*>(sd) : nullptr;   // MXFP4 scales are already applied
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, nrows, s.H, kparts, part, fsd, y);
     return hipGetLastError();
-  };
-  using B = std::bool_constant<false>;
-  using F8 = std::bool_constant<true>;
-  using M1 = std::integral_constant<int, 1>;
-  using M2 = std::integral_constant<int, 2>;
-  using M4 = std::integral_constant<int, 4>;
-  if (s.fp8) return bm == 16 ? go(F8{}, M1{}) : bm == 32 ? go(F8{}, M2{}) : go(F8{}, M4{});
-  return bm == 16 ? go(B{}, M1{}) : bm == 32 ? go(B{}, M2{}) : go(B{}, M4{});
+  });
 }
 
 }  // namespace beam

@@ -246,6 +246,7 @@ bool use_tiled(const Shape& s, int T) {
   // a single expert gives the tiled kernels only ceil(T/288) row tiles: below ~1k
   // tokens the streaming kernels (64-row tiles, k-split down) fill the chip better
   if (s.dense && T <= 1024) return false;
+  if (s.mx) return false;   // MXFP4 weights run on the streaming kernels at every T
   const long mean = ((long)T * s.K) / s.E;
   return mean >= 32 && s.H % kTN == 0 && s.I % 128 == 0;
 }

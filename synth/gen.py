@@ -57,7 +57,7 @@ class Workload:
     sigma_router: float
     sigma_expert: float
     bias: str           # "zero" | "balanced" | "skew"
-    weight: str         # "bf16" | "fp8"
+    weight: str         # "bf16" | "fp8" | "mxfp4"
     weights_id: int     # seed id of the expert weights: every real-shape workload shares one layer
 
     def with_T(self, T: int) -> "Workload":
@@ -80,6 +80,12 @@ WORKLOADS = {
     # real shape, e4m3 expert weights + per-output-channel fp32 scales
     "fp8_decode": _real("fp8_decode", 5, 32, weight="fp8"),
     "fp8_prefill": _real("fp8_prefill", 5, 2048, weight="fp8"),
+    # real shape, MXFP4 expert weights (E2M1 codes, one E8M0 scale per 32 inputs)
+    "mxfp4_decode": _real("mxfp4_decode", 10, 64, weight="mxfp4"),
+    "mxfp4_prefill": _real("mxfp4_prefill", 10, 2048, weight="mxfp4"),
+    # tiny MXFP4 layers (the MXFP4 kernels need H and I to be multiples of 256)
+    "tiny_mx": Workload("tiny_mx", 11, 64, 256, 256, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "mxfp4", 11),
+    "dense_tiny_mx": Workload("dense_tiny_mx", 12, 64, 256, 512, 1, 1, 1, 1, 1.0, 0.05, 0.02, "zero", "mxfp4", 12),
     # speculative verification: 8 sequences x (1 + 15 drafted tokens) in one forward pass
     "spec_verify": _real("spec_verify", 6, 128),
     # dense SwiGLU MLP (the first layers): one "expert" of intermediate 20480 = 8 x 2560
@@ -212,10 +218,19 @@ def expert_matrix(w: Workload, seed: int, which: str, e: int):
 
     which: "gate" | "up" -> [I, H]; "down" -> [H, I].
     bf16 workloads return uint16 bit patterns; fp8 workloads return
-    (uint8 e4m3 codes, fp32 scale [out]) with scale = max|w| / 448 per row.
+    (uint8 e4m3 codes, fp32 scale [out]) with scale = max|w| / 448 per row;
+    mxfp4 workloads return (packed E2M1 codes [out, in/2], E8M0 scales [out, in/32]).
     """
     tid = {"gate": WG_ID, "up": WU_ID, "down": WD_ID}[which]
     shape = (w.inter, w.hidden) if which in ("gate", "up") else (w.hidden, w.inter)
+    if w.weight == "mxfp4":
+        # random E2M1 codes (two per byte) and random E8M0 block scales near sigma / 2.25
+        # (2.25 = mean |value| of a uniform code): drawn directly, nothing is quantised here
+        g = _rng(seed, w.weights_id, tid, e)
+        packed = g.integers(0, 256, (shape[0], shape[1] // 2), dtype=np.uint8)
+        e0 = 127 + int(np.floor(np.log2(w.sigma_expert / 2.25)))
+        scales = (e0 + g.integers(-1, 2, (shape[0], shape[1] // 32))).astype(np.uint8)
+        return packed, scales
     a = _rng(seed, w.weights_id, tid, e).standard_normal(shape, dtype=np.float32)
     a *= np.float32(w.sigma_expert)
     if w.weight == "bf16":
@@ -263,15 +278,22 @@ def device_expert_weights(w: Workload, seed: int, device, threads: Optional[int]
     """All E experts' matrices as device tensors, generated on the host expert by expert.
 
     Returns dict(gate, up, down) of [E, out, in] tensors (bf16, or uint8 e4m3
-    codes) and, for fp8, s_gate, s_up, s_down [E, out] fp32 scales.
+    codes) and, for fp8, s_gate, s_up, s_down [E, out] fp32 scales; for mxfp4,
+    [E, out, in/2] packed codes and [E, out, in/32] uint8 E8M0 scales.
     """
     E = w.n_experts
     fp8 = w.weight == "fp8"
-    wdt = torch.uint8 if fp8 else torch.bfloat16
-    out = {"gate": torch.empty(E, w.inter, w.hidden, dtype=wdt, device=device),
-           "up": torch.empty(E, w.inter, w.hidden, dtype=wdt, device=device),
-           "down": torch.empty(E, w.hidden, w.inter, dtype=wdt, device=device)}
+    mx = w.weight == "mxfp4"
+    wdt = torch.uint8 if (fp8 or mx) else torch.bfloat16
+    div = 2 if mx else 1
+    out = {"gate": torch.empty(E, w.inter, w.hidden // div, dtype=wdt, device=device),
+           "up": torch.empty(E, w.inter, w.hidden // div, dtype=wdt, device=device),
+           "down": torch.empty(E, w.hidden, w.inter // div, dtype=wdt, device=device)}
     scales = {}
+    if mx:
+        scales = {"s_gate": torch.empty(E, w.inter, w.hidden // 32, dtype=torch.uint8, device=device),
+                  "s_up": torch.empty(E, w.inter, w.hidden // 32, dtype=torch.uint8, device=device),
+                  "s_down": torch.empty(E, w.hidden, w.inter // 32, dtype=torch.uint8, device=device)}
     if fp8:
         scales = {"s_gate": torch.empty(E, w.inter, dtype=torch.float32, device=device),
                   "s_up": torch.empty(E, w.inter, dtype=torch.float32, device=device),
@@ -287,7 +309,7 @@ def device_expert_weights(w: Workload, seed: int, device, threads: Optional[int]
     done = 0
     with ThreadPoolExecutor(threads) as ex:
         for (which, e), v in ex.map(one, keys):
-            if fp8:
+            if fp8 or mx:
                 q, sc = v
                 out[which][e].copy_(torch.from_numpy(q))
                 scales["s_" + which][e].copy_(torch.from_numpy(sc))

@@ -48,7 +48,7 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 def cfg_of(w):
     import sparse_moe_layer_top_amd as bm
     return bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha,
-                     bm.W_FP8_E4M3 if w.weight == "fp8" else bm.W_BF16)
+                     {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight])
 
 
 def guarded(w, seed=0):

@@ -17,13 +17,13 @@ HEADER = os.path.join(ROOT, "include", "beam_moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(beam_moe_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(beam_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_three_entry_points():
     names = declared_functions()
     for n in ("beam_moe_route", "beam_moe_permute", "beam_moe_forward", "beam_moe_workspace_bytes",
-              "beam_moe_status_string"):
+              "beam_moe_status_string", "beam_moe_block_forward", "beam_dense_mlp_forward", "beam_mxfp4_quantize"):
         assert n in names
 
 
@@ -50,7 +50,9 @@ BAD_CONFIGS = [
     (dict(topk_groups=1, n_groups=64, top_k=8), B.ERR_INVALID),   # K > Gk*E/G = 4
     (dict(routed_scale=float("inf")), B.ERR_INVALID),
     (dict(weight_type=3), B.ERR_INVALID),
-    (dict(hidden=5100), B.ERR_UNSUPPORTED),               # not a multiple of 64
+    (dict(hidden=5100), B.ERR_UNSUPPORTED),               # not a multiple of 128
+    (dict(hidden=5248, weight_type=B.W_MXFP4), B.ERR_UNSUPPORTED),   # MXFP4: not a multiple of 256
+    (dict(inter=2688, weight_type=B.W_MXFP4), B.ERR_UNSUPPORTED),
     (dict(n_experts=512, n_groups=8), B.ERR_UNSUPPORTED),
     (dict(top_k=9, topk_groups=4), B.ERR_UNSUPPORTED),
     (dict(n_groups=128, n_experts=256, topk_groups=8), B.ERR_UNSUPPORTED),
@@ -212,3 +214,48 @@ def test_dense_workspace_holds_h_and_the_split_partials():
     small = bm.beam_dense_workspace_bytes(cfg, 64)
     assert small >= 64 * cfg.inter * 2 + 2 * 64 * cfg.hidden * 4       # h plus at least two fp32 parts
     assert bm.beam_dense_workspace_bytes(cfg, 8192) >= 8192 * cfg.inter * 2
+
+
+def test_mxfp4_scales_required_and_byte_aligned():
+    c = ctypes.byref(_cfg(weight_type=B.W_MXFP4))
+    f = FAKE
+    need = bm.beam_moe_workspace_bytes(bm.Config(weight_type=B.W_MXFP4), 4)
+    # MXFP4 without block scales: invalid
+    assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, None, None, None, f, None, None, f, need, None) == B.ERR_INVALID
+    # a byte-aligned scale pointer is not an error for MXFP4 (it would be for fp8): the call gets past
+    # validation and fails only at the workspace check
+    odd = ctypes.c_void_p(0x10001)
+    assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, odd, odd, odd, f, None, None, f, need - 1, None) == B.ERR_WORKSPACE
+    c8 = ctypes.byref(_cfg(weight_type=B.W_FP8_E4M3))
+    assert B.LIB.beam_moe_forward(c8, 4, f, f, None, f, f, f, odd, odd, odd, f, None, None, f, need - 1, None) == B.ERR_INVALID
+    cd = ctypes.byref(_dcfg(weight_type=B.W_MXFP4))
+    assert B.LIB.beam_dense_mlp_forward(cd, 4, f, f, f, f, None, None, None, f, f, 1 << 40, None) == B.ERR_INVALID
+    n = ctypes.c_size_t(0)
+    assert B.LIB.beam_dense_workspace_bytes(ctypes.byref(_dcfg(inter=20480 + 128, weight_type=B.W_MXFP4)), 4,
+                                            ctypes.byref(n)) == B.ERR_UNSUPPORTED
+
+
+def test_mxfp4_quantize_validation():
+    L, f = B.LIB, FAKE
+    assert L.beam_mxfp4_quantize(4, 48, f, f, f, None) == B.ERR_INVALID          # cols % 32
+    assert L.beam_mxfp4_quantize(-1, 64, f, f, f, None) == B.ERR_INVALID
+    assert L.beam_mxfp4_quantize(4, -32, f, f, f, None) == B.ERR_INVALID
+    assert L.beam_mxfp4_quantize(4, 64, None, f, f, None) == B.ERR_INVALID
+    assert L.beam_mxfp4_quantize(4, 64, f, f, None, None) == B.ERR_INVALID
+    assert L.beam_mxfp4_quantize(4, 64, ctypes.c_void_p(0x10008), f, f, None) == B.ERR_INVALID   # misaligned
+    assert L.beam_mxfp4_quantize(0, 64, None, None, None, None) == B.OK                        # no-op
+    assert L.beam_mxfp4_quantize(4, 0, None, None, None, None) == B.OK
+
+
+def test_binding_checks_mxfp4_shapes():
+    """The binding's shape checks run before any device work: CPU tensors fail on the device check, so a
+    wrong shape must be reported first."""
+    import torch
+    E, H, I = 2, 256, 256
+    cfg = bm.Config(hidden=H, inter=I, n_experts=E, n_groups=1, topk_groups=1, top_k=1, weight_type=B.W_MXFP4)
+    wg = torch.empty(E, I, H, dtype=torch.uint8)                   # unpacked width: wrong for MXFP4
+    with pytest.raises(ValueError, match=r"w_gate: expected shape \(2, 256, 128\)"):
+        B._expert_weights(cfg.weight_type, (E,), H, I, wg, wg, wg, None, None, None, None)
+    sc = torch.empty(E, I, H // 32, dtype=torch.float32)
+    with pytest.raises(TypeError, match="expected torch.uint8"):
+        B._need(sc, "s_gate", torch.uint8, (E, I, H // 32))

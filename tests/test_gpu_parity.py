@@ -146,13 +146,14 @@ _WEIGHTS = {}
 
 def real_weights(kind):
     if kind not in _WEIGHTS:
-        w = gen.workload("decode" if kind == "bf16" else "fp8_decode")
+        w = gen.workload({"bf16": "decode", "fp8": "fp8_decode", "mxfp4": "mxfp4_decode"}[kind])
         C.say(f"generating {kind} expert weights (256 experts, real shape)")
         _WEIGHTS[kind] = gen.device_expert_weights(w, 0, C.dev(), log=C.say)
     return _WEIGHTS[kind]
 
 
-REAL = [("decode", 8), ("prefill", 4), ("skew", 4), ("fp8_decode", 8), ("fp8_prefill", 4)]
+REAL = [("decode", 8), ("prefill", 4), ("skew", 4), ("fp8_decode", 8), ("fp8_prefill", 4), ("mxfp4_decode", 8),
+        ("mxfp4_prefill", 4)]
 
 
 @pytest.mark.parametrize("name,n_sample", REAL)
