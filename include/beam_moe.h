@@ -134,7 +134,7 @@ int beam_moe_permute(const beam_moe_config* cfg, int32_t T, const int32_t* topk_
  *   w_gate, w_up   [device] [E, I, H] bf16; e4m3 bytes (FP8); [E, I, H/2] packed E2M1 bytes (MXFP4)
  *   w_down         [device] [E, H, I] bf16; e4m3 (FP8); [E, H, I/2] packed E2M1 (MXFP4)
  *   s_gate, s_up   [device] FP8: [E, I] fp32 per-output-channel scales; MXFP4: [E, I, H/32]
- *                  E8M0 bytes; BF16: NULL.  FP8 scales 4-byte aligned.
+ *                  E8M0 bytes; BF16: NULL.  FP8 scales 4-byte aligned, MXFP4 scales 16-byte.
  *   s_down         [device] FP8: [E, H] fp32; MXFP4: [E, H, I/32] E8M0 bytes; BF16: NULL
  *                  an FP8 weight's value is decode(q) * scale[e, out]; an MXFP4
  *                  weight's is e2m1(q) * 2^(scale[e, out, in/32] - 127)
@@ -236,7 +236,7 @@ int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* 
 
 /*   x              [device] [T, H] bf16
  *   w_gate, w_up   [device] [I, H] bf16; e4m3 bytes with s_gate, s_up [I] fp32; or MXFP4
- *                  [I, H/2] with s_gate, s_up [I, H/32] E8M0 bytes
+ *                  [I, H/2] with s_gate, s_up [I, H/32] E8M0 bytes (16-byte aligned)
  *   w_down         [device] [H, I] bf16; e4m3 with s_down [H] fp32; or MXFP4 [H, I/2] with [H, I/32]
  *   out            [device] [T, H] bf16 out
  *   workspace      [device] beam_dense_workspace_bytes bytes

@@ -119,7 +119,8 @@ int check_forward_args(const beam_moe_config* cfg, const void* x, const float* w
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
       !aligned16(out) || (b_router && !aligned4(b_router)) || (topk_ids_out && !aligned4(topk_ids_out)) ||
       (topk_w_out && !aligned4(topk_w_out)) ||
-      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))) ||
+      (cfg->weight_type == BEAM_MOE_W_MXFP4 && (!aligned16(s_gate) || !aligned16(s_up) || !aligned16(s_down))))
     return BEAM_MOE_ERR_INVALID;
   return BEAM_MOE_OK;
 }
@@ -399,7 +400,8 @@ int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const 
   if (scaled != (s_gate != nullptr) || scaled != (s_up != nullptr) || scaled != (s_down != nullptr))
     return BEAM_MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) ||
-      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))))
+      (cfg->weight_type == BEAM_MOE_W_FP8_E4M3 && (!aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down))) ||
+      (cfg->weight_type == BEAM_MOE_W_MXFP4 && (!aligned16(s_gate) || !aligned16(s_up) || !aligned16(s_down))))
     return BEAM_MOE_ERR_INVALID;
   const Shape s = dense_shape(cfg);
   const DenseLayout L = dense_layout(s, T);

@@ -10,9 +10,11 @@
 // Work unit: one row tile of an expert (from the device-built tile list) times
 // a block of output columns.  Each wave streams its weight rows straight from
 // HBM into MFMA B-fragments (16 columns x 8 consecutive k per lane, 16-byte
-// loads), so no LDS round trip sits between HBM and the matrix cores.  The
-// reduction order inside an MFMA fragment is free, so A (x or h) and B use the
-// same lane -> k mapping: lane l holds k in [k0 + 8*(l/16), +8), row/column l%16.
+// loads), so no LDS round trip sits between HBM and the matrix cores; the
+// activation rows (x or h), the same for the workgroup's four waves, reach the
+// MFMAs through a small LDS window.  The reduction order inside an MFMA
+// fragment is free, so A and B use the same lane -> k mapping: lane l holds k
+// in [k0 + 8*(l/16), +8), row/column l%16.
 //
 // FP8 weights (OCP e4m3) are converted exactly to bf16 in registers; the
 // per-output-channel scale multiplies the fp32 accumulator in the epilogue.
@@ -66,84 +68,156 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Scale bytes of a window: D consecutive k-steps x 4 lane quads, one byte each, contiguous in an
+// MXFP4 scale row, fetched with one D-dword load.
+template <int D>
+struct ScaleVec;
+template <>
+struct ScaleVec<1> { using T = uint32_t; };
+template <>
+struct ScaleVec<2> { using T = u32x2; };
+template <>
+struct ScaleVec<4> { using T = u32x4; };
+
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);   // s_waitcnt lgkmcnt(0), vmcnt not waited on
+
+// Activation fragments of one window: D steps x MT row blocks x SK/32 MFMA k-slices, each 1 KB
+// (64 lanes x 16 bytes, laid out so that lane l reads slot[l]: conflict-free).  The four waves of a
+// workgroup share one copy; wave w loads fragments w, w+4, ... (past F it reloads a valid one
+// into a spare slot, so every wave runs the same straight-line code).
+template <int WT, int MT, int D>
+struct AWin {
+  static constexpr int NA = WFrag<WT>::SK / 32;
+  static constexpr int F = D * MT * NA;
+  static constexpr int FW = (F + 3) / 4;
+  static constexpr int SLOTS = 4 * FW;
+};
+
 // The streaming k-loop shared by both kernels.  A step covers SK k-values.
 // Lane (row/column l%16, quad q = l/16) owns k in [step*SK + q*SK/4, +SK/4):
 // one 16-byte weight load per weight block (NB blocks of 16 output columns)
-// and SK/32 16-byte activation loads per row block (MT blocks of 16 rows);
-// wrow/arow already include the lane's quad offset.
+// per step; wrow/arow already include the lane's quad offset, srow (MXFP4) is
+// the row's scale base.
 //
-// Loads go out in bursts: a window of D steps is issued back to back (so each
-// weight row sees D*64 contiguous bytes requested together, which HBM serves
-// better than the same loads spread out), and windows are double-buffered:
-// window w+1 is in flight while window w feeds the MFMAs.  sched_barrier
-// fences keep the compiler from reordering the bursts.  nsteps must be a
-// multiple of 2*D (the caller picks D so): a remainder loop after the
-// pipelined one makes the compiler schedule the whole loop worse.
+// Weights go straight from HBM into registers in bursts: a window of D steps
+// is issued back to back (each weight row sees D*64 contiguous bytes requested
+// together, which HBM serves better than the same loads spread out), and
+// windows are double-buffered: window w+1 is in flight while window w feeds
+// the MFMAs.  Activations (L2 hits, the same for every wave of the workgroup)
+// do not sit in registers for a whole window: each wave loads a quarter of
+// the next window's fragments into a few staging registers together with the
+// weight burst, writes them to LDS after computing the current window, and
+// one barrier per window publishes them.  That keeps per-lane registers to
+// the weight ring, which sets how many bytes each CU keeps in flight.
+// sched_barrier fences keep the compiler from reordering the bursts.
 template <int WT, int MT, int NB, int D>
-__device__ __forceinline__ void stream_k(int nsteps, const typename WFrag<WT>::E* const (&wrow)[NB],
+__device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const typename WFrag<WT>::E* const (&wrow)[NB],
                                          const uint8_t* const (&srow)[NB], const uint16_t* const (&arow)[MT],
-                                         f32x4 (&acc)[MT][NB]) {
+                                         u32x4 (*lds)[AWin<WT, MT, D>::SLOTS][kWave], f32x4 (&acc)[MT][NB]) {
   using W = WFrag<WT>;
-  constexpr int SK = W::SK, SE = W::SE, NA = SK / 32;
+  using A = AWin<WT, MT, D>;
+  constexpr int SK = W::SK, SE = W::SE, NA = A::NA;
+  const int q = lane / 16;
+  const uint16_t* mine[A::FW];   // this lane's address of each fragment this wave loads (window 0)
+#pragma unroll
+  for (int i = 0; i < A::FW; ++i) {
+    const int f = (wave + 4 * i) % A::F;
+    const int fj = f / (MT * NA), fm = (f / NA) % MT, fa = f % NA;
+    const uint16_t* p = arow[0];
+#pragma unroll
+    for (int m = 1; m < MT; ++m) p = fm == m ? arow[m] : p;
+    mine[i] = p + fj * SK + fa * 8;
+  }
   u32x4 wb[2][D][NB];
-  uint32_t sb[2][D][W::kBlockScale ? NB : 1];
-  bf16x8 ab[2][D][MT][NA];
+  uint32_t sb[2][W::kBlockScale ? NB : 1][D];
+  u32x4 st[A::FW];
   const int nwin = nsteps / D;
   auto load = [&](int buf, int w) {
     const int base = min(w, nwin - 1) * D;   // past the end: reload the last window (unused)
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
+    for (int i = 0; i < A::FW; ++i) st[i] = *reinterpret_cast<const u32x4*>(mine[i] + base * SK);
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SE);
+    if constexpr (W::kBlockScale) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SE);
-        if constexpr (W::kBlockScale) sb[buf][j][nb] = srow[nb][(base + j) * (SK / 32)];
+        const auto v = *reinterpret_cast<const typename ScaleVec<D>::T*>(srow[nb] + base * 4);
+        if constexpr (D == 1) {
+          sb[buf][nb][0] = v;
+        } else {
+#pragma unroll
+          for (int j = 0; j < D; ++j) sb[buf][nb][j] = v[j];
+        }
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int a = 0; a < NA; ++a)
-          ab[buf][j][mt][a] = *reinterpret_cast<const bf16x8*>(arow[mt] + (base + j) * SK + a * 8);
     }
+  };
+  auto publish = [&](int buf) {   // staged fragments -> LDS, then every wave's are visible
+#pragma unroll
+    for (int i = 0; i < A::FW; ++i) lds[buf][wave + 4 * i][lane] = st[i];
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   auto compute = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < D; ++j)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float sc = W::kBlockScale ? e8m0_to_f32(sb[buf][j][W::kBlockScale ? nb : 0]) : 1.f;
+        float sc = 1.f;
+        if constexpr (W::kBlockScale) sc = e8m0_to_f32((sb[buf][nb][j] >> (8 * q)) & 0xFFu);
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
           const bf16x8 b = W::frag(wb[buf][j][nb], a, sc);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][nb] = mfma16(ab[buf][j][mt][a], b, acc[mt][nb]);
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 af = __builtin_bit_cast(bf16x8, lds[buf][(j * MT + mt) * NA + a][lane]);
+            acc[mt][nb] = mfma16(af, b, acc[mt][nb]);
+          }
         }
       }
   };
   load(0, 0);
+  publish(0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int w = 0; w < nwin; w += 2) {
+  for (int w = 0; w + 1 < nwin; w += 2) {
     load(1, w + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    publish(1);
     __builtin_amdgcn_sched_barrier(0);
     load(0, w + 2);
     __builtin_amdgcn_sched_barrier(0);
     compute(1);
     __builtin_amdgcn_sched_barrier(0);
+    publish(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (nwin & 1) compute(0);   // odd window count: the last window is in buffer 0
 }
 
-// Burst depth cap by register budget: 2*D*(NB + MT*SK/32) 16-byte registers per lane.
+// Columns per wave (G blocks of 16 per matrix) and the burst-depth caps, per
+// weight type and row-tile count, from sweeps of the real shapes at T = 64,
+// 512 and 2048: depth 4 wins at 16-row tiles for every weight type (bf16
+// gate/up 6.1 TB/s), 2 at 64-row tiles; one column block per wave wherever
+// measured.
 template <int WT, int MT>
-struct MaxDepth {
-  static constexpr int value = WT == kWMX ? (MT == 1 ? 2 : 1)
-                                          : (MT == 1 ? 4 : (MT == 2 ? (WT == kWFP8 ? 2 : 4) : (WT == kWFP8 ? 1 : 2)));
+struct StreamShape {
+  static constexpr int kGateUpG = 1;
+  static constexpr int kDownG = 1;
+  static constexpr int kGateUpDepth = MT == 4 ? 2 : (WT == kWFP8 && MT == 2 ? 2 : 4);
+  static constexpr int kDownDepth = MT == 4 ? 2 : (MT == 2 && WT != kWBF16 ? 2 : 4);
 };
 
-// gate/up: grid (max_tiles, I/64), 4 waves; wave w owns columns [64*by + 16*w, +16) of gate and up.
-// Rows past the tile's end read a valid row (the tile's first) and their
-// outputs are discarded: an MFMA output row depends only on its own A row.
-template <int WT, int MT, int D>
+// gate/up: grid (max_tiles, ceil(I / 64G)), 4 waves; wave w owns columns
+// [64G*by + 16G*w, +16G) of gate and of up.  Rows past the tile's end read a
+// valid row (the tile's first) and their outputs are discarded: an MFMA
+// output row depends only on its own A row.  Waves past the last column
+// stream valid rows (the workgroup shares a barrier) and store nothing.
+template <int WT, int MT, int G, int D>
 __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K, const uint16_t* __restrict__ x,
                                                             const void* __restrict__ wg, const void* __restrict__ wu,
                                                             const void* __restrict__ sg, const void* __restrict__ su,
@@ -153,14 +227,17 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
                                                             const int32_t* __restrict__ ntiles,
                                                             uint16_t* __restrict__ h) {
   using W = WFrag<WT>;
+  __shared__ u32x4 lds[2][AWin<WT, MT, D>::SLOTS][kWave];
   const int tile = blockIdx.x;
-  if (tile >= ntiles[0]) return;
+  if (tile >= ntiles[0]) return;   // uniform over the workgroup
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int lo = offsets[e];
   const int rows = min(offsets[e + 1] - lo - r0, 16 * MT);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int l16 = lane % 16, q = lane / 16;
-  const int col = blockIdx.y * 64 + wave * 16 + l16;
+  const int colw = blockIdx.y * 64 * G + wave * 16 * G;
+  const bool active = colw < I;
+  const int col0 = active ? colw : 0;
   const int qa = q * (W::SK / 4), qw = q * (W::SE / 4);   // lane quad offsets: activations (k), weights (E units)
 
   const uint16_t* xr[MT];
@@ -171,42 +248,50 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
     xr[mt] = x + (size_t)tok * H + qa;
   }
   using WE = typename W::E;
-  const size_t row = (size_t)e * I + col;
-  const size_t wrow = row * ((size_t)H * W::SE / W::SK) + qw;
-  const WE* const wr[2] = {static_cast<const WE*>(wg) + wrow, static_cast<const WE*>(wu) + wrow};
-  const uint8_t* sr[2] = {nullptr, nullptr};
-  if constexpr (W::kBlockScale) {
-    const size_t srow = row * (H / 32) + q;
-    sr[0] = static_cast<const uint8_t*>(sg) + srow;
-    sr[1] = static_cast<const uint8_t*>(su) + srow;
-  }
-  f32x4 acc[MT][2];
+  const WE* wr[2 * G];
+  const uint8_t* sr[2 * G];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2, D>(H / W::SK, wr, sr, xr, acc);
+  for (int g = 0; g < 2 * G; ++g) {
+    const size_t row = (size_t)e * I + col0 + (g % G) * 16 + l16;
+    wr[g] = static_cast<const WE*>(g < G ? wg : wu) + row * ((size_t)H * W::SE / W::SK) + qw;
+    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) + row * (H / 32) : nullptr;
+  }
+  f32x4 acc[MT][2 * G];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_k<WT, MT, 2 * G, D>(H / W::SK, wave, lane, wr, sr, xr, lds, acc);
+  if (!active) return;
 
-  float scg = 1.f, scu = 1.f;
-  if constexpr (WT == kWFP8) {
-    scg = static_cast<const float*>(sg)[row];
-    scu = static_cast<const float*>(su)[row];
-  }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int g = 0; g < G; ++g) {
+    const int col = col0 + g * 16 + l16;
+    float scg = 1.f, scu = 1.f;
+    if constexpr (WT == kWFP8) {
+      scg = static_cast<const float*>(sg)[(size_t)e * I + col];
+      scu = static_cast<const float*>(su)[(size_t)e * I + col];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = mt * 16 + q * 4 + i;   // MFMA output row of this lane's i-th value
-      if (r < rows) {
-        const float g = acc[mt][0][i] * scg, u = acc[mt][1][i] * scu;
-        h[(size_t)(lo + r0 + r) * I + col] = f32_to_bf16(silu(g) * u);
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + q * 4 + i;   // MFMA output row of this lane's i-th value
+        if (r < rows) {
+          const float gv = acc[mt][g][i] * scg, uv = acc[mt][G + g][i] * scu;
+          h[(size_t)(lo + r0 + r) * I + col] = f32_to_bf16(silu(gv) * uv);
+        }
       }
     }
   }
 }
 
-// With kparts > 1 (grid z), part z covers reduction steps [z*n, (z+1)*n) and
-// writes its raw fp32 sums to part[z][row][col]; splitk_reduce_kernel adds the
-// parts in z order.  Used when one expert's rows are too few to fill the chip.
-template <int WT, int MT, int D>
+// down: grid (max_tiles, ceil(H / 128G), kparts); wave w owns columns
+// [128G*by + 32G*w, +32G).  With kparts > 1 (grid z), part z covers reduction
+// steps [z*n, (z+1)*n) and writes its raw fp32 sums to part[z][row][col];
+// splitk_reduce_kernel adds the parts in z order.  Used when one expert's rows
+// are too few to fill the chip.
+template <int WT, int MT, int G, int D>
 __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const uint16_t* __restrict__ hbuf,
                                                           const void* __restrict__ wd, const void* __restrict__ sd,
                                                           const int32_t* __restrict__ offsets,
@@ -215,74 +300,60 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
                                                           uint16_t* __restrict__ y, int kparts, int nrows,
                                                           float* __restrict__ part) {
   using W = WFrag<WT>;
+  __shared__ u32x4 lds[2][AWin<WT, MT, D>::SLOTS][kWave];
   const int tile = blockIdx.x;
-  if (tile >= ntiles[0]) return;
+  if (tile >= ntiles[0]) return;   // uniform over the workgroup
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int lo = offsets[e];
   const int rows = min(offsets[e + 1] - lo - r0, 16 * MT);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int l16 = lane % 16, q = lane / 16;
-  const int c0 = blockIdx.y * 128 + wave * 32;
-  if (c0 >= H) return;   // wave-uniform; H % 32 == 0 so both 16-column blocks are in range
+  const int cw = blockIdx.y * 128 * G + wave * 32 * G;
+  const bool active = cw < H;
+  const int c0 = active ? cw : 0;
   const int qa = q * (W::SK / 4), qw = q * (W::SE / 4);
+  const int nsteps = I / W::SK / kparts;
+  const size_t zs = (size_t)blockIdx.z * nsteps;   // first step of this part (0 unless split)
 
   const uint16_t* hr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
-    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + qa;
+    hr[mt] = hbuf + (size_t)(lo + r0 + (r < rows ? r : 0)) * I + qa + zs * W::SK;
   }
   using WE = typename W::E;
   const size_t IE = (size_t)I * W::SE / W::SK;          // a weight row in E units
-  const size_t row0 = (size_t)e * H + c0 + l16;
-  const WE* wr[2] = {static_cast<const WE*>(wd) + row0 * IE + qw, static_cast<const WE*>(wd) + (row0 + 16) * IE + qw};
-  const uint8_t* sr[2] = {nullptr, nullptr};
-  if constexpr (W::kBlockScale) {
-    sr[0] = static_cast<const uint8_t*>(sd) + row0 * (I / 32) + q;
-    sr[1] = static_cast<const uint8_t*>(sd) + (row0 + 16) * (I / 32) + q;
+  const WE* wr[2 * G];
+  const uint8_t* sr[2 * G];
+#pragma unroll
+  for (int g = 0; g < 2 * G; ++g) {
+    const size_t row = (size_t)e * H + c0 + g * 16 + l16;
+    wr[g] = static_cast<const WE*>(wd) + row * IE + qw + zs * W::SE;
+    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(sd) + row * (I / 32) + zs * (W::SK / 32) : nullptr;
   }
-  f32x4 acc[MT][2];
+  f32x4 acc[MT][2 * G];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nsteps = I / W::SK / kparts;
-  if (kparts > 1) {
-    const size_t zs = (size_t)blockIdx.z * nsteps;       // first step of this part
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) hr[mt] += zs * W::SK;
-    const WE* const wk[2] = {wr[0] + zs * W::SE, wr[1] + zs * W::SE};
-    const uint8_t* const sk[2] = {sr[0] ? sr[0] + zs * (W::SK / 32) : nullptr, sr[1] ? sr[1] + zs * (W::SK / 32) : nullptr};
-    stream_k<WT, MT, 2, D>(nsteps, wk, sk, hr, acc);
+    for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_k<WT, MT, 2 * G, D>(nsteps, wave, lane, wr, sr, hr, lds, acc);
+  if (!active) return;
+
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int g = 0; g < 2 * G; ++g) {
+    const int col = c0 + g * 16 + l16;
+    float sc = 1.f;
+    if constexpr (WT == kWFP8) sc = static_cast<const float*>(sd)[(size_t)e * H + col];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + q * 4 + i;
-        if (r < rows) {
-          float* pr = part + ((size_t)blockIdx.z * nrows + lo + r0 + r) * H + c0 + l16;
-          pr[0] = acc[mt][0][i];
-          pr[16] = acc[mt][1][i];
-        }
-      }
-    return;
-  }
-  const WE* const wk[2] = {wr[0], wr[1]};
-  const uint8_t* const sk[2] = {sr[0], sr[1]};
-  stream_k<WT, MT, 2, D>(nsteps, wk, sk, hr, acc);
-
-  float s0 = 1.f, s1 = 1.f;
-  if constexpr (WT == kWFP8) {
-    s0 = static_cast<const float*>(sd)[row0];
-    s1 = static_cast<const float*>(sd)[row0 + 16];
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = mt * 16 + q * 4 + i;
-      if (r < rows) {
-        uint16_t* yr = y + (size_t)(lo + r0 + r) * H + c0 + l16;
-        yr[0] = f32_to_bf16(acc[mt][0][i] * s0);
-        yr[16] = f32_to_bf16(acc[mt][1][i] * s1);
+        if (r >= rows) continue;
+        if (kparts > 1)
+          part[((size_t)blockIdx.z * nrows + lo + r0 + r) * H + col] = acc[mt][g][i];
+        else
+          y[(size_t)(lo + r0 + r) * H + col] = f32_to_bf16(acc[mt][g][i] * sc);
       }
     }
   }
@@ -296,29 +367,30 @@ int expert_tile_rows(const Shape& s, int T) {
   return 64;
 }
 
-// Largest D in {4, 2, 1}, at most cap, with nsteps a multiple of 2*D (nsteps is even).
+// Largest D in {4, 2, 1}, at most cap, dividing nsteps.  (An MXFP4 scale
+// window of D dwords is then aligned: a scale row holds 4 * nsteps bytes.)
 static int pick_depth(int nsteps, int cap) {
   for (int d = cap; d > 1; d /= 2)
-    if (nsteps % (2 * d) == 0) return d;
+    if (nsteps % d == 0) return d;
   return 1;
 }
 
-template <int WT, int MT, int D>
+template <int WT, int MT, int G, int D>
 static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const void* sg,
                                 const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                                 const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, D>), dim3(max_tiles, s.I / 64), dim3(256), 0, stream, s.H, s.I,
-                     s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h);
+  hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, G, D>), dim3(max_tiles, (s.I + 64 * G - 1) / (64 * G)), dim3(256),
+                     0, stream, s.H, s.I, s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h);
   return hipGetLastError();
 }
 
-template <int WT, int MT, int D>
+template <int WT, int MT, int G, int D>
 static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd, const void* sd,
                               const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                               uint16_t* y, int kparts, int nrows, float* part, hipStream_t stream) {
-  hipLaunchKernelGGL((down_stream_kernel<WT, MT, D>), dim3(max_tiles, (s.H + 127) / 128, kparts), dim3(256), 0,
-                     stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part);
+  hipLaunchKernelGGL((down_stream_kernel<WT, MT, G, D>), dim3(max_tiles, (s.H + 128 * G - 1) / (128 * G), kparts),
+                     dim3(256), 0, stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part);
   return hipGetLastError();
 }
 
@@ -353,15 +425,14 @@ static int steps_per_k(const Shape& s, int K) {
 }
 
 // Reduction parts for the dense path's down GEMM: the fewest parts giving about
-// 1024 workgroups, each part an even number of steps (a multiple of 8 where the
-// step count allows, keeping the deepest burst schedule); 1 when the row tiles
-// alone fill the GPU.
+// 1024 workgroups, each part a multiple of 4 steps where the step count allows
+// (keeping the deepest burst schedule); 1 when the row tiles alone fill the GPU.
 int down_kparts(const Shape& s, int T) {
   if (!s.dense || use_tiled(s, T)) return 1;
   const int bm = expert_tile_rows(s, T);
   const long wgs = (long)((T + bm - 1) / bm) * ((s.H + 127) / 128);
   const int steps = steps_per_k(s, s.I);
-  const int grain = steps % 8 == 0 ? 8 : 2;
+  const int grain = steps % 4 == 0 ? 4 : (steps % 2 == 0 ? 2 : 1);
   int best = 1;
   for (int k = 1; k <= 32 && k * grain <= steps; ++k) {
     if (steps % (k * grain)) continue;
@@ -372,9 +443,8 @@ int down_kparts(const Shape& s, int T) {
 }
 
 // Dispatch on (weight type, row-tile count, depth).
-template <int WT, int MT, typename F>
+template <int cap, typename F>
 static hipError_t with_depth(int nsteps, F&& f) {
-  constexpr int cap = MaxDepth<WT, MT>::value;
   switch (pick_depth(nsteps, cap)) {
     case 4: return f(std::integral_constant<int, (cap >= 4 ? 4 : 1)>{});
     case 2: return f(std::integral_constant<int, (cap >= 2 ? 2 : 1)>{});
@@ -405,9 +475,9 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
   return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
     constexpr int WT = decltype(wt)::value;
     constexpr int M = decltype(mt)::value;
-    return with_depth<WT, M>(s.H / WFrag<WT>::SK, [&](auto d) {
-      return gateup_launch<WT, M, decltype(d)::value>(s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles,
-                                                      max_tiles, h, stream);
+    return with_depth<StreamShape<WT, M>::kGateUpDepth>(s.H / WFrag<WT>::SK, [&](auto d) {
+      return gateup_launch<WT, M, StreamShape<WT, M>::kGateUpG, decltype(d)::value>(
+          s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
     });
   });
 }
@@ -421,9 +491,10 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
   return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
     constexpr int WT = decltype(wt)::value;
     constexpr int M = decltype(mt)::value;
-    hipError_t err = with_depth<WT, M>(s.I / WFrag<WT>::SK / kparts, [&](auto d) {
-      return down_launch<WT, M, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, kparts, nrows,
-                                                    part, stream);
+    hipError_t err = with_depth<StreamShape<WT, M>::kDownDepth>(s.I / WFrag<WT>::SK / kparts, [&](auto d) {
+      return down_launch<WT, M, StreamShape<WT, M>::kDownG, decltype(d)::value>(s, h, wd, sd, offsets, tiles, ntiles,
+                                                                                 max_tiles, y, kparts, nrows, part,
+                                                                                 stream);
     });
     if (err != hipSuccess || kparts == 1) return err;
     const size_t n4 = (size_t)nrows * s.H / 4;

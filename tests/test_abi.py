@@ -216,17 +216,20 @@ def test_dense_workspace_holds_h_and_the_split_partials():
     assert bm.beam_dense_workspace_bytes(cfg, 8192) >= 8192 * cfg.inter * 2
 
 
-def test_mxfp4_scales_required_and_byte_aligned():
+def test_mxfp4_scales_required_and_aligned():
     c = ctypes.byref(_cfg(weight_type=B.W_MXFP4))
     f = FAKE
     need = bm.beam_moe_workspace_bytes(bm.Config(weight_type=B.W_MXFP4), 4)
     # MXFP4 without block scales: invalid
     assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, None, None, None, f, None, None, f, need, None) == B.ERR_INVALID
-    # a byte-aligned scale pointer is not an error for MXFP4 (it would be for fp8): the call gets past
-    # validation and fails only at the workspace check
-    odd = ctypes.c_void_p(0x10001)
-    assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, odd, odd, odd, f, None, None, f, need - 1, None) == B.ERR_WORKSPACE
+    # MXFP4 scale rows are read in 16-byte pieces: a 16-byte aligned scale pointer passes validation
+    # (the call then fails only at the workspace check), a 4-byte aligned one does not (fp8 accepts it)
+    four = ctypes.c_void_p(0x10004)
+    assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, f, f, f, f, None, None, f, need - 1, None) == B.ERR_WORKSPACE
+    assert B.LIB.beam_moe_forward(c, 4, f, f, None, f, f, f, four, four, four, f, None, None, f, need - 1, None) == B.ERR_INVALID
     c8 = ctypes.byref(_cfg(weight_type=B.W_FP8_E4M3))
+    assert B.LIB.beam_moe_forward(c8, 4, f, f, None, f, f, f, four, four, four, f, None, None, f, need - 1, None) == B.ERR_WORKSPACE
+    odd = ctypes.c_void_p(0x10001)
     assert B.LIB.beam_moe_forward(c8, 4, f, f, None, f, f, f, odd, odd, odd, f, None, None, f, need - 1, None) == B.ERR_INVALID
     cd = ctypes.byref(_dcfg(weight_type=B.W_MXFP4))
     assert B.LIB.beam_dense_mlp_forward(cd, 4, f, f, f, f, None, None, None, f, f, 1 << 40, None) == B.ERR_INVALID
