@@ -46,20 +46,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"stream": ("experts.hip", "common.h"), "tiled": ("experts_tiled.hip", "common.h")}
+
+
+def kernel_source_hash(kind):
+    """Hash of the sources of the gate/up kernel family ("stream" or "tiled")."""
     h = hashlib.sha256()
-    for f in ("experts.hip", "experts_tiled.hip", "common.h"):
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_top_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, kernel):
+def load_traffic(workload, kernel, kind):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(kind):
         return None
     return d.get("bytes_per_launch")
 
@@ -252,7 +256,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(w.name, "gateup")
+    roof["traffic"] = load_traffic(w.name, "gateup", "tiled" if tiled else "stream")
     roof["kernel"] = "tiled_kernel<gateup>" if tiled else "gateup_stream_kernel"
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flops_per_launch"] = gu_flops

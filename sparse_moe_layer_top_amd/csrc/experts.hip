@@ -133,7 +133,7 @@ __device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const t
   u32x4 st[A::FW];
   const int nwin = nsteps / D;
   auto load = [&](int buf, int w) {
-    const int base = min(w, nwin - 1) * D;   // past the end: reload the last window (unused)
+    const int base = w * D;
 #pragma unroll
     for (int i = 0; i < A::FW; ++i) st[i] = *reinterpret_cast<const u32x4*>(mine[i] + base * SK);
 #pragma unroll
@@ -182,7 +182,8 @@ __device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const t
   load(0, 0);
   publish(0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int w = 0; w + 1 < nwin; w += 2) {
+  int w = 0;
+  for (; w + 2 < nwin; w += 2) {
     load(1, w + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(0);
@@ -196,7 +197,18 @@ __device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const t
     publish(0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (nwin & 1) compute(0);   // odd window count: the last window is in buffer 0
+  // the last one or two windows, with nothing loaded past the end
+  if (w + 1 < nwin) {
+    load(1, w + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    publish(1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+  } else {
+    compute(0);
+  }
 }
 
 // Columns per wave (G blocks of 16 per matrix) and the burst-depth caps, per
