@@ -13,10 +13,14 @@ in this setting, so every tensor is drawn from a fixed distribution:
     W_down       ~ N(0, 0.02) -> bf16         [E, H, I]
     fp8 workloads: the same fp32 draw, quantised per output channel to OCP e4m3
     with scale = max_in |w| / 448 (fp32).
+    MXFP4 workloads: uniform random bytes as E2M1 code pairs, and E8M0 block
+    scales 127 + floor(log2(0.02 / 2.25)) + {-1, 0, 1} (2.25 = mean |E2M1 value|),
+    so the weights have about the bf16 draws' scale; nothing is quantised.
+    norm gains (the norms around the block): 1 + N(0, 0.1^2), fp32 [2, H].
 
 Every tensor comes from its own stream, numpy.random.default_rng(
 [seed, workload_id, tensor_id, index]); tensor ids: 0 x, 1 W_router, 2 bias,
-3 W_gate, 4 W_up, 5 W_down, 6 re-drawn x rows.  Expert matrices are drawn one
+3 W_gate, 4 W_up, 5 W_down, 6 re-drawn x rows, 7 norm gains.  Expert matrices are drawn one
 expert at a time, so any single expert can be regenerated on the CPU without
 touching the rest.  All real-shape workloads share one layer's expert weights
 (workload id 2 in their seed); the fp8 workloads quantise those same fp32
