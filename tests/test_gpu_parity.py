@@ -179,6 +179,49 @@ def test_real_shape_forward(name, n_sample):
     C.say(f"[{name}] max rel {mx:.2e} mean|d|/rms {mn:.2e}")
 
 
+def test_real_shape_max_tokens():
+    """The largest T the ABI accepts, 262,144 tokens (2M (token, slot) pairs, about 8K rows per
+    expert: the tiled kernels with some 29 row tiles per expert), balanced routing.  Ids and
+    weights bit-exact / to 1e-5 for every token whose oracle score gaps clear the guard; the
+    others (near-ties, not re-drawn at this size) must still be valid selections; outputs on
+    sampled tokens."""
+    import sparse_moe_layer_top_amd as bm
+    w = gen.workload("prefill", bm.MAX_TOKENS)
+    spec = oracle.LayerSpec.of(w)
+    C.say(f"[max tokens] T={w.T} inputs")
+    x, wr, b = gen.router_inputs(w, 0)
+    W = real_weights("bf16")
+    C.say("[max tokens] forward on the GPU")
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ids, wts = ids.cpu().numpy(), wts.cpu().numpy()
+    C.say("[max tokens] oracle routing in chunks")
+    near = []
+    chunk = 16384
+    for s0 in range(0, w.T, chunk):
+        sl = slice(s0, min(s0 + chunk, w.T))
+        rid, rw = oracle.route(spec, x[sl], wr, b)
+        bad = oracle.gap_violations(spec, x[sl], wr, b)
+        ok = np.ones(len(rid), bool)
+        ok[bad] = False
+        C.check_ids_w(ids[sl][ok], wts[sl][ok], rid[ok], rw[ok])
+        near.extend((s0 + bad).tolist())
+    near = np.asarray(near, np.int64)
+    C.say(f"[max tokens] {len(near)} near-tie tokens checked for validity only")
+    if len(near):
+        sel = ids[near]
+        assert np.all(np.diff(sel, axis=1) > 0) and sel.min() >= 0 and sel.max() < w.n_experts
+        assert np.allclose(wts[near].sum(axis=1), w.alpha, rtol=1e-5)
+    rng = np.random.default_rng(77)
+    cand = np.setdiff1d(np.concatenate([[0, w.T - 1], rng.choice(w.T, 8, replace=False)]), near)
+    src = gen.ExpertSource(w, 0)
+    src.prefetch(np.unique(ids[cand]))
+    C.say(f"[max tokens] oracle forward on {len(cand)} sampled tokens")
+    ref = oracle.forward(spec, x[cand], wr, b, src.get)
+    assert np.array_equal(ref["ids"], ids[cand])
+    mx, mn = C.check_out(C.bits_of(out)[cand], ref["out"])
+    C.say(f"[max tokens] max rel {mx:.2e} mean|d|/rms {mn:.2e}")
+
+
 @pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
 def test_real_shape_permute(name):
     import sparse_moe_layer_top_amd as bm
