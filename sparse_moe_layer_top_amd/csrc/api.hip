@@ -44,20 +44,18 @@ Shape shape_of(const beam_moe_config* c) {
   return s;
 }
 
-// Router K-split: kc = H/ks is a multiple of 32, between 128 and 1280 where
-// possible (short fp32 chains), and the grid should reach ~1024 workgroups.
+// Router K-split: ks parts of kc = H/ks (a multiple of the 32-wide MFMA step),
+// the fewest giving about 1024 workgroups of 128 tokens x 64 experts, each
+// part at least 4 steps long where H allows.
 int choose_ks(const Shape& s, int T) {
   const int units = s.H / 32;
-  const long blocks0 = (long)((T + 63) / 64) * ((s.E + 63) / 64);
+  const long tiles = (long)((T + 127) / 128) * ((s.E + 63) / 64);
   int best = 1;
   for (int ks = 1; ks <= units; ++ks) {
     if (units % ks) continue;
-    const int kc = s.H / ks;
-    if (kc > 1280) continue;
-    if (kc < 128 && best != 1) break;
+    if (units / ks < 4 && best > 1) break;
     best = ks;
-    if (blocks0 * ks >= 1024) break;
-    if (kc <= 128) break;
+    if (tiles * ks >= 1024) break;
   }
   return best;
 }

@@ -8,79 +8,120 @@
 // "Residual stream").
 //
 // Two kernels:
-//   router_logits: z partial sums over a K-split of the hidden dim, fp32 FMA,
-//                  LDS-staged 64-token x 64-expert tiles;
+//   router_logits: z partial sums over a K-split of the hidden dim on bf16
+//                  MFMA: W_router (fp32) is split exactly into three bf16
+//                  planes, w = hi + mid + lo, so every product x*w-part is
+//                  exact (x is bf16) and the sums accumulate in fp32;
 //   router_select: one workgroup per token: sum the partials in a fixed order,
 //                  add the bias, sigmoid, then the selection in one wave.
 #include "common.h"
 
 namespace beam {
 
-constexpr int kRTok = 64, kRExp = 64, kRK = 32;
+constexpr int kRTok = 128;   // tokens per workgroup: 4 waves x 2 row blocks of 16
+constexpr int kRExp = 64;    // experts per workgroup: 4 column blocks of 16
+constexpr int kRK = 32;      // k per step (one 16x16x32 MFMA)
+constexpr int kRRow = 40;    // LDS row of one expert's 32 k: 32 bf16 + 8 pad (80 bytes: conflict-free reads)
 
+// w = hi + mid + lo exactly, each a bf16: hi keeps w's top 8 significand bits
+// (truncation), mid the top 8 of the remainder, lo the rest (at most 8
+// significant bits).  Both subtractions are exact.  (Holds for |w| >= 2^-100;
+// below that lo may lose bits to the fp32 subnormal range.)
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t h = __float_as_uint(w) & 0xFFFF0000u;
+  const float r1 = __fsub_rn(w, __uint_as_float(h));
+  const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = __fsub_rn(r1, __uint_as_float(m));
+  hi = h >> 16;
+  mid = m >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+// grid (ceil(T/128), ceil(E/64), ks); part ks covers k in [ks*kc, (ks+1)*kc), kc a multiple of 32.
+// Wave w owns tokens [t0 + 32w, +32) and all 64 experts of the tile: per 32-k
+// step two x fragments (straight from global memory: a lane reads 8
+// consecutive k of one token row) and 3 planes x 4 expert blocks of W_router
+// fragments from LDS, 24 MFMAs.  Each thread stages one expert x 8 k of the
+// next step (8 loads, coalesced across the wave's 64 experts), splits them and
+// writes the three planes; the LDS stage is double-buffered.
 __global__ __launch_bounds__(256) void router_logits_kernel(int T, int H, int E, int kc,
                                                             const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) float xs[kRK][kRTok + 4];
-  __shared__ __attribute__((aligned(16))) float ws[kRK][kRExp + 4];
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][3][kRExp][kRRow];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l16 = lane % 16, q = lane / 16;
   const int t0 = blockIdx.x * kRTok, e0 = blockIdx.y * kRExp, ks = blockIdx.z;
-  const int kbeg = ks * kc, kend = kbeg + kc;
-  const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  const int kbeg = ks * kc, nst = kc / kRK;
 
-  const int lt = tid / 4, lp = tid % 4;   // x tile: token, 8-wide k part
-  const int wk = tid / 8, wp = tid % 8;   // w tile: k row, 8-wide expert part
-  const bool xok = (t0 + lt) < T;
-  const uint16_t* xrow = x + (size_t)(xok ? t0 + lt : 0) * H;
-  const bool wvec = (E % 4) == 0 && (e0 + wp * 8 + 8) <= E;
-
-  for (int k0 = kbeg; k0 < kend; k0 += kRK) {
-    // stage x (bf16 -> fp32, transposed to [k][token]) and W_router ([k][expert])
-    u32x4 xv = {0u, 0u, 0u, 0u};
-    if (xok) xv = *reinterpret_cast<const u32x4*>(xrow + k0 + lp * 8);
+  const uint16_t* xr[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = min(t0 + wave * 32 + m * 16 + l16, T - 1);   // rows past T read a valid row, never stored
+    xr[m] = x + (size_t)t * H + kbeg + q * 8;
+  }
+  const int be = tid % kRExp, bk = (tid / kRExp) * 8;          // staged expert and first k of this thread
+  const bool eok = e0 + be < E;
+  const float* wcol = wr + (size_t)(kbeg + bk) * E + min(e0 + be, E - 1);
+  float wv[8];
+  auto load_b = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = eok ? wcol[((size_t)st * kRK + j) * E] : 0.f;
+  };
+  auto store_b = [&](int buf) {
+    u32x4 pl[3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      xs[lp * 8 + 2 * j][lt] = __uint_as_float(xv[j] << 16);
-      xs[lp * 8 + 2 * j + 1][lt] = __uint_as_float(xv[j] & 0xFFFF0000u);
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3(wv[2 * j], h0, m0, l0);
+      split3(wv[2 * j + 1], h1, m1, l1);
+      pl[0][j] = h0 | (h1 << 16);
+      pl[1][j] = m0 | (m1 << 16);
+      pl[2][j] = l0 | (l1 << 16);
     }
-    const float* wrow = wr + (size_t)(k0 + wk) * E + e0 + wp * 8;
-    if (wvec) {
-      f32x4 a = *reinterpret_cast<const f32x4*>(wrow);
-      f32x4 b = *reinterpret_cast<const f32x4*>(wrow + 4);
-      *reinterpret_cast<f32x4*>(&ws[wk][wp * 8]) = a;
-      *reinterpret_cast<f32x4*>(&ws[wk][wp * 8 + 4]) = b;
-    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ws[wk][wp * 8 + j] = (e0 + wp * 8 + j < E) ? wrow[j] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < kRK; ++k) {
-      f32x4 a = *reinterpret_cast<const f32x4*>(&xs[k][ty * 4]);
-      f32x4 b = *reinterpret_cast<const f32x4*>(&ws[k][tx * 4]);
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(&ws[buf][p][be][bk]) = pl[p];
+  };
+
+  f32x4 acc[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_b(0);
+  store_b(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load_b(st + 1);
+    bf16x8 a[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) a[m] = *reinterpret_cast<const bf16x8*>(xr[m] + st * kRK);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&ws[buf][p][n * 16 + l16][q * 8]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b, acc[m][n], 0, 0, 0);
+      }
+    if (st + 1 < nst) store_b(buf ^ 1);   // buffer buf^1 was last read in step st-1, before the barrier
     __syncthreads();
   }
+  // C[r][c] of a 16x16 block sits in lane (c = l%16, r = 4q + i)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) partial[((size_t)ks * T + t) * E + e] = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + wave * 32 + m * 16 + q * 4 + i;
+      if (t >= T) continue;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int e = e0 + n * 16 + l16;
+        if (e < E) partial[((size_t)ks * T + t) * E + e] = acc[m][n][i];
+      }
     }
-  }
 }
 
 // 64-bit max across the wave (keys are unique, so the result is exact).
