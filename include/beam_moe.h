@@ -167,14 +167,17 @@ int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T,
  * Beam 1.0 overview, section "Residual stream", which fixes the norms to FP32;
  * RMSNorm with a per-channel gain is the reading, the only norm the pages name):
  *   out[t,h] = bf16( (x[t,h] * r_t) * gamma[h] ),  r_t = 1 / sqrt( ss_t / H + eps )
- * where ss_t is the FP32 sum of x[t,h]^2 over h in index order and every step is
- * one correctly rounded FP32 operation, so the result is reproducible bit for bit.
+ * where ss_t is the FP32 sum of x[t,h]^2 in a fixed order (the channels form 64
+ * contiguous blocks of whole 8-channel chunks, block l holding chunks
+ * [l*n/64, (l+1)*n/64), n = H/8; each block summed in channel order, then the
+ * block sums in block order) and every step is one correctly rounded FP32
+ * operation, so the result is reproducible bit for bit.
  *   hidden     H: multiple of 8, at most BEAM_MOE_MAX_NORM_HIDDEN
  *   x          [device] [T, H] bf16
  *   gamma      [device] [H] fp32 (4-byte aligned)
  *   eps        finite, > 0
  *   out        [device] [T, H] bf16 out; may be the same buffer as x
- * Latency is one sequential H-term FP32 chain per token (tokens run in parallel). */
+ * Latency per token: an (H/64)-term chain per lane plus a 64-term chain (tokens run in parallel). */
 int beam_moe_rms_norm(int32_t T, int32_t hidden, const void* x, const float* gamma, float eps, void* out,
                       void* stream);
 

@@ -17,10 +17,16 @@ Readings this module takes where the pages are silent:
   * the norm is RMSNorm with a learned per-channel gain (the only norm the pages
     name, on queries and keys) and an additive epsilon inside the square root:
         n = v / sqrt(mean(v^2) + eps),  out = n * gamma;
-  * "in FP32" is taken literally, one IEEE float32 operation per step in the
-    order of the definition: the sum of squares runs over the channels in index
-    order, then one correctly rounded division by H, one addition of eps, one
-    correctly rounded square root and one reciprocal; then v * r, then * gamma;
+  * "in FP32" is taken literally, one IEEE float32 operation per step: the sum
+    of squares in float32, then one correctly rounded division by H, one
+    addition of eps, one correctly rounded square root and one reciprocal; then
+    v * r, then * gamma;
+  * the pages fix the precision of the sum, not its order.  The order taken:
+    the H channels form 64 contiguous blocks of whole 8-channel chunks (block
+    l holds chunks [l*n/64, (l+1)*n/64), n = H/8, integer division), each
+    block summed in channel order, then the 64 block sums added in block
+    order.  (Any fixed order is an FP32 sum; this one is 64-way parallel, where
+    a single channel-order chain is H dependent additions long.);
   * the stream, the MoE output and both norm outputs are bf16 (the model dtype),
     each norm output rounded once to nearest-even;
   * the mix is new = bf16( f32(a * stream) + f32(b * post) ) with the weights
@@ -40,21 +46,43 @@ from .codecs import bf16_round_bits, bf16_to_f64
 from .moe import LayerSpec, forward
 
 
+NORM_BLOCKS = 64
+
+
+def norm_block_bounds(H: int):
+    """Channel ranges [lo, hi) of the 64 summation blocks of an H-channel row (H % 8 == 0)."""
+    if H % 8:
+        raise ValueError("the norm takes rows of a multiple of 8 channels")
+    n = H // 8
+    return [(8 * (l * n // NORM_BLOCKS), 8 * ((l + 1) * n // NORM_BLOCKS)) for l in range(NORM_BLOCKS)]
+
+
+def sum_squares_f32(v) -> np.ndarray:
+    """float32 sum of squares of float32 rows [T, H] in the block order above."""
+    v = np.asarray(v, np.float32)
+    T, H = v.shape
+    total = np.zeros(T, np.float32)
+    for lo, hi in norm_block_bounds(H):
+        part = np.zeros(T, np.float32)
+        for h in range(lo, hi):                  # one block, channel order
+            part = part + v[:, h] * v[:, h]      # float32 * float32 and + float32: one rounding each
+        total = total + part                     # block sums in block order
+    return total
+
+
 def rms_norm_bits(v_bits, gamma, eps: float) -> np.ndarray:
     """RMSNorm of bf16 rows [T, H] with float32 gain gamma [H] -> bf16 bits [T, H].
 
-    Sum of squares in float32, channel by channel in index order; then
-    ms = ss / H, r = 1 / sqrt(ms + eps), out = bf16((v * r) * gamma), each step
-    one float32 operation.
+    Sum of squares in float32 (sum_squares_f32); then ms = ss / H,
+    r = 1 / sqrt(ms + eps), out = bf16((v * r) * gamma), each step one float32
+    operation.
     """
     v = bf16_to_f64(np.asarray(v_bits, np.uint16)).astype(np.float32)
     if v.ndim == 1:
         v = v[None, :]
     T, H = v.shape
     g = np.asarray(gamma, np.float32)
-    ss = np.zeros(T, np.float32)
-    for h in range(H):                       # the sequential float32 sum the definition states
-        ss = ss + v[:, h] * v[:, h]          # float32 * float32 and + float32: one rounding each
+    ss = sum_squares_f32(v)
     ms = ss / np.float32(H)
     r = np.float32(1.0) / np.sqrt(ms + np.float32(eps))
     n = v * r[:, None]

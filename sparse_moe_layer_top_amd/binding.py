@@ -262,7 +262,8 @@ def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_rou
 
 def beam_moe_rms_norm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out: Optional[torch.Tensor] = None):
     """RMSNorm of bf16 rows x [T,H] with fp32 gain gamma [H]: bf16((x * r) * gamma), r = 1/sqrt(mean(x^2)+eps),
-    every step one correctly rounded fp32 operation (sum of squares in channel order).  out may be x."""
+    every step one correctly rounded fp32 operation (sum of squares over 64 contiguous channel blocks, each in
+    channel order, then the block sums in block order).  out may be x."""
     T, H = x.shape
     dev = x.device
     _need(x, "x", torch.bfloat16, (T, H))

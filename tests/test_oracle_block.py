@@ -47,6 +47,27 @@ def test_rms_norm_within_one_ulp_of_exact(sigma, eps, H):
     assert np.all(got[~nz] == 0)
 
 
+def test_sum_squares_block_order():
+    """The stated order, by hand: a big square first, then unit squares.  Channel order would
+    absorb every +1 into 2^24 (ties to even); the block order first sums each block's units
+    exactly and adds the block sums, which survive.  H = 5120: blocks of 80 channels, so the
+    big value in channel 79 (the last of block 0) leaves blocks 1..63 with 80 units each; a
+    block boundary one channel off gives a different total."""
+    v = np.zeros((1, 5120), np.float32)
+    v[0, 79] = 4096.0                      # square 2^24
+    v[0, 80:] = 1.0
+    assert block.norm_block_bounds(5120)[:2] == [(0, 80), (80, 160)]
+    assert block.sum_squares_f32(v)[0] == np.float32(2.0 ** 24 + 63 * 80)
+    seq = np.float32(0)
+    for h in range(5120):
+        seq = np.float32(seq + v[0, h] * v[0, h])
+    assert seq == np.float32(2.0 ** 24)    # what channel order would give
+    # fewer than 64 chunks: empty blocks add nothing; every chunk is summed exactly once
+    w = np.arange(1, 25, dtype=np.float32)[None, :] / 8
+    assert block.sum_squares_f32(w)[0] == np.float32(np.sum(np.float64(w) ** 2))
+    assert sum(hi - lo for lo, hi in block.norm_block_bounds(24)) == 24
+
+
 def test_rms_norm_constant_rows_closed_form():
     H = 256
     v = _bf16(np.full((2, H), 0.5))
