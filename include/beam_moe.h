@@ -233,8 +233,8 @@ typedef struct {
 } beam_dense_config;
 
 /* Workspace bytes of beam_dense_mlp_forward for T tokens (host only, pure): the
- * row-tile list, h [T, I] bf16 and, when the down GEMM is split over the
- * reduction to fill the GPU (small T), its fp32 partial sums. */
+ * row-tile list, h [T, I] bf16 and, when the GEMMs are split over the
+ * reduction to fill the GPU (small T), their fp32 partial sums. */
 int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* bytes);
 
 /*   x              [device] [T, H] bf16
@@ -243,7 +243,8 @@ int beam_dense_workspace_bytes(const beam_dense_config* cfg, int32_t T, size_t* 
  *   w_down         [device] [H, I] bf16; e4m3 with s_down [H] fp32; or MXFP4 [H, I/2] with [H, I/32]
  *   out            [device] [T, H] bf16 out
  *   workspace      [device] beam_dense_workspace_bytes bytes
- * Deterministic: a split reduction adds its parts in a fixed order. */
+ * Deterministic: a split reduction adds its parts in a fixed order (for gate/up,
+ * before the SwiGLU). */
 int beam_dense_mlp_forward(const beam_dense_config* cfg, int32_t T, const void* x,
                            const void* w_gate, const void* w_up, const void* w_down,
                            const void* s_gate, const void* s_up, const void* s_down,

@@ -160,7 +160,7 @@ int run_forward(const Shape& s, const Layout& L, int T, const uint16_t* xb, cons
                                     beam::expert_tile_rows(s, T), tiles, ntiles, hs));
   BEAM_TRY_HIP(mark(3));
   BEAM_TRY_HIP(beam::launch_gateup(s, T, xb, w_gate, w_up, s_gate, s_up, offsets, sorted, tiles, ntiles,
-                                   L.max_tiles, h, hs));
+                                   L.max_tiles, 1, nullptr, h, hs));
   BEAM_TRY_HIP(mark(4));
   BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, 1, nullptr, y, hs));
   BEAM_TRY_HIP(mark(5));
@@ -193,13 +193,14 @@ Shape dense_shape(const beam_dense_config* c) {
 
 struct DenseLayout {
   size_t offsets, sorted, tiles, ntiles, h, part, total;
-  int max_tiles, tile_rows, kparts;
+  int max_tiles, tile_rows, gkparts, kparts;
 };
 
 DenseLayout dense_layout(const Shape& s, int T) {
   DenseLayout L{};
   L.tile_rows = beam::expert_tile_rows(s, T);
   L.max_tiles = (T + L.tile_rows - 1) / L.tile_rows + 1;
+  L.gkparts = beam::gateup_kparts(s, T);
   L.kparts = beam::down_kparts(s, T);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -212,7 +213,10 @@ DenseLayout dense_layout(const Shape& s, int T) {
   L.tiles = take((size_t)L.max_tiles * 8);
   L.ntiles = take(4);
   L.h = take((size_t)T * s.I * 2);
-  if (L.kparts > 1) L.part = take((size_t)L.kparts * T * s.H * 4);
+  // fp32 partial sums of the split GEMMs (gate/up's are consumed before down runs: one region)
+  const size_t gpart = L.gkparts > 1 ? (size_t)L.gkparts * T * 2 * s.I * 4 : 0;
+  const size_t dpart = L.kparts > 1 ? (size_t)L.kparts * T * s.H * 4 : 0;
+  if (gpart || dpart) L.part = take(std::max(gpart, dpart));
   L.total = off;
   return L;
 }
@@ -410,7 +414,7 @@ int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const 
   int32_t* tiles = at<int32_t>(workspace, L.tiles);
   int32_t* ntiles = at<int32_t>(workspace, L.ntiles);
   uint16_t* h = at<uint16_t>(workspace, L.h);
-  float* part = L.kparts > 1 ? at<float>(workspace, L.part) : nullptr;
+  float* part = (L.kparts > 1 || L.gkparts > 1) ? at<float>(workspace, L.part) : nullptr;
   auto mark = [&](int i) -> hipError_t {
     return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), hs) : hipSuccess;
   };
@@ -418,7 +422,7 @@ int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const 
   BEAM_TRY_HIP(beam::launch_dense_setup(T, L.tile_rows, offsets, sorted, tiles, ntiles, hs));
   BEAM_TRY_HIP(mark(1));
   BEAM_TRY_HIP(beam::launch_gateup(s, T, static_cast<const uint16_t*>(x), w_gate, w_up, s_gate, s_up, offsets, sorted,
-                                   tiles, ntiles, L.max_tiles, h, hs));
+                                   tiles, ntiles, L.max_tiles, L.gkparts, part, h, hs));
   BEAM_TRY_HIP(mark(2));
   BEAM_TRY_HIP(beam::launch_down(s, T, h, w_down, s_down, offsets, tiles, ntiles, L.max_tiles, L.kparts, part,
                                  static_cast<uint16_t*>(out), hs));

@@ -84,8 +84,8 @@ hipError_t launch_permute(const Shape& s, int T, const int32_t* ids, int nchunks
                           int tile_rows, int32_t* tiles, int32_t* ntiles, hipStream_t stream);
 hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
                          const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
-                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
-                         hipStream_t stream);
+                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, int kparts, float* part,
+                         uint16_t* h, hipStream_t stream);
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part,
@@ -93,6 +93,7 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
 hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float* w,
                           const int32_t* pair_to_row, uint16_t* out, hipStream_t stream);
 int down_kparts(const Shape& s, int T);
+int gateup_kparts(const Shape& s, int T);
 hipError_t launch_mxfp4_quantize(int rows, int cols, const uint16_t* w, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 hipError_t launch_dense_setup(int T, int tile_rows, int32_t* offsets, int32_t* sorted_pairs, int32_t* tiles,

@@ -224,8 +224,10 @@ struct StreamShape {
   static constexpr int kDownDepth = MT == 4 ? 2 : (MT == 2 && WT != kWBF16 ? 2 : 4);
 };
 
-// gate/up: grid (max_tiles, ceil(I / 64G)), 4 waves; wave w owns columns
-// [64G*by + 16G*w, +16G) of gate and of up.  Rows past the tile's end read a
+// gate/up: grid (max_tiles, ceil(I / 64G), kparts), 4 waves; wave w owns columns
+// [64G*by + 16G*w, +16G) of gate and of up.  With kparts > 1 part z covers
+// reduction steps [z*n, (z+1)*n) and writes raw fp32 sums; swiglu_reduce_kernel
+// adds the parts in z order and applies the SwiGLU (the dense path at small T).  Rows past the tile's end read a
 // valid row (the tile's first) and their outputs are discarded: an MFMA
 // output row depends only on its own A row.  Waves past the last column
 // stream valid rows (the workgroup shares a barrier) and store nothing.
@@ -237,7 +239,8 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
                                                             const int32_t* __restrict__ sorted_pairs,
                                                             const int32_t* __restrict__ tiles,
                                                             const int32_t* __restrict__ ntiles,
-                                                            uint16_t* __restrict__ h) {
+                                                            uint16_t* __restrict__ h, int kparts, int nrows,
+                                                            float* __restrict__ part) {
   using W = WFrag<WT>;
   __shared__ u32x4 lds[2][AWin<WT, MT, D>::SLOTS][kWave];
   const int tile = blockIdx.x;
@@ -251,13 +254,15 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   const bool active = colw < I;
   const int col0 = active ? colw : 0;
   const int qa = q * (W::SK / 4), qw = q * (W::SE / 4);   // lane quad offsets: activations (k), weights (E units)
+  const int nsteps = H / W::SK / kparts;
+  const size_t zs = (size_t)blockIdx.z * nsteps;   // first step of this part (0 unless split)
 
   const uint16_t* xr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + l16;
     const int tok = sorted_pairs[lo + r0 + (r < rows ? r : 0)] / K;
-    xr[mt] = x + (size_t)tok * H + qa;
+    xr[mt] = x + (size_t)tok * H + qa + zs * W::SK;
   }
   using WE = typename W::E;
   const WE* wr[2 * G];
@@ -265,16 +270,32 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
 #pragma unroll
   for (int g = 0; g < 2 * G; ++g) {
     const size_t row = (size_t)e * I + col0 + (g % G) * 16 + l16;
-    wr[g] = static_cast<const WE*>(g < G ? wg : wu) + row * ((size_t)H * W::SE / W::SK) + qw;
-    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) + row * (H / 32) : nullptr;
+    wr[g] = static_cast<const WE*>(g < G ? wg : wu) + row * ((size_t)H * W::SE / W::SK) + qw + zs * W::SE;
+    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) + row * (H / 32) + zs * (W::SK / 32)
+                           : nullptr;
   }
   f32x4 acc[MT][2 * G];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2 * G, D>(H / W::SK, wave, lane, wr, sr, xr, lds, acc);
+  stream_k<WT, MT, 2 * G, D>(nsteps, wave, lane, wr, sr, xr, lds, acc);
   if (!active) return;
+  if (kparts > 1) {   // raw fp32 sums of this part: gate at part[z][row][col], up at part[z][row][I + col]
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + q * 4 + i;
+          if (r >= rows) continue;
+          float* pr = part + ((size_t)blockIdx.z * nrows + lo + r0 + r) * (2 * (size_t)I) + col0 + g * 16 + l16;
+          pr[0] = acc[mt][g][i];
+          pr[I] = acc[mt][G + g][i];
+        }
+    return;
+  }
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -391,10 +412,47 @@ template <int WT, int MT, int G, int D>
 static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const void* sg,
                                 const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                                 const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, G, D>), dim3(max_tiles, (s.I + 64 * G - 1) / (64 * G)), dim3(256),
-                     0, stream, s.H, s.I, s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h);
+                                int kparts, int nrows, float* part, hipStream_t stream) {
+  hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, G, D>), dim3(max_tiles, (s.I + 64 * G - 1) / (64 * G), kparts),
+                     dim3(256), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h,
+                     kparts, nrows, part);
   return hipGetLastError();
+}
+
+// h[row][c] = bf16( SiLU(G * sg[c]) * (U * su[c]) ), G and U the sums of the
+// parts in z order (fp8: the per-row scales; NULL: none).  The dense path's
+// single expert: the scale of intermediate column c is sg[c] / su[c].
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(int nrows, int I, int kparts, const float* __restrict__ part,
+                                                            const float* __restrict__ sg, const float* __restrict__ su,
+                                                            uint16_t* __restrict__ h) {
+  const size_t n = (size_t)nrows * I, stride = (size_t)nrows * 2 * I;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (size_t)gridDim.x * 256 * 4) {
+    const size_t row = i / I, c = i % I;
+    const float* pg = part + row * 2 * I + c;
+    f32x4 g = *reinterpret_cast<const f32x4*>(pg), u = *reinterpret_cast<const f32x4*>(pg + I);
+    for (int z = 1; z < kparts; ++z) {
+      const f32x4 gz = *reinterpret_cast<const f32x4*>(pg + z * stride);
+      const f32x4 uz = *reinterpret_cast<const f32x4*>(pg + z * stride + I);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g[j] = __fadd_rn(g[j], gz[j]);
+        u[j] = __fadd_rn(u[j], uz[j]);
+      }
+    }
+    u32x2 o;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float hv[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int cc = (int)c + 2 * j + m;
+        const float gv = g[2 * j + m] * (sg ? sg[cc] : 1.f), uv = u[2 * j + m] * (su ? su[cc] : 1.f);
+        hv[m] = silu(gv) * uv;
+      }
+      o[j] = static_cast<uint32_t>(f32_to_bf16(hv[0])) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16);
+    }
+    *reinterpret_cast<u32x2*>(h + i) = o;
+  }
 }
 
 template <int WT, int MT, int G, int D>
@@ -454,6 +512,22 @@ int down_kparts(const Shape& s, int T) {
   return best;
 }
 
+// Reduction parts for the dense path's gate/up GEMM, chosen like the down GEMM's.
+int gateup_kparts(const Shape& s, int T) {
+  if (!s.dense || use_tiled(s, T)) return 1;
+  const int bm = expert_tile_rows(s, T);
+  const long wgs = (long)((T + bm - 1) / bm) * ((s.I + 63) / 64);
+  const int steps = steps_per_k(s, s.H);
+  const int grain = steps % 4 == 0 ? 4 : (steps % 2 == 0 ? 2 : 1);
+  int best = 1;
+  for (int k = 1; k <= 32 && k * grain <= steps; ++k) {
+    if (steps % (k * grain)) continue;
+    best = k;
+    if (wgs * k >= 1024) break;
+  }
+  return best;
+}
+
 // Dispatch on (weight type, row-tile count, depth).
 template <int cap, typename F>
 static hipError_t with_depth(int nsteps, F&& f) {
@@ -479,18 +553,27 @@ static hipError_t dispatch_wt_mt(const Shape& s, int bm, G&& go) {
 
 hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
                          const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
-                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
-                         hipStream_t stream) {
+                         const int32_t* tiles, const int32_t* ntiles, int max_tiles, int kparts, float* part,
+                         uint16_t* h, hipStream_t stream) {
   if (use_tiled(s, T))
     return launch_gateup_tiled(s, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
                                sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+  const int nrows = T * s.K;
   return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
     constexpr int WT = decltype(wt)::value;
     constexpr int M = decltype(mt)::value;
-    return with_depth<StreamShape<WT, M>::kGateUpDepth>(s.H / WFrag<WT>::SK, [&](auto d) {
+    hipError_t err = with_depth<StreamShape<WT, M>::kGateUpDepth>(s.H / WFrag<WT>::SK / kparts, [&](auto d) {
       return gateup_launch<WT, M, StreamShape<WT, M>::kGateUpG, decltype(d)::value>(
-          s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+          s, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, kparts, nrows, part, stream);
     });
+    if (err != hipSuccess || kparts == 1) return err;
+    const size_t n4 = (size_t)nrows * s.I / 4;
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
+    const float* fsg = WT == kWFP8 ? static_cast<const float*>(sg) : nullptr;   // MXFP4 scales are already applied
+    const float* fsu = WT == kWFP8 ? static_cast<const float*>(su) : nullptr;
+    hipLaunchKernelGGL(swiglu_reduce_kernel, dim3(blocks), dim3(256), 0, stream, nrows, s.I, kparts, part, fsg, fsu,
+                       h);
+    return hipGetLastError();
   });
 }
 
