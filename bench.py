@@ -265,6 +265,37 @@ def main():
     roof["mfma_TFLOPs"] = round(tfs, 1)
     roof["mfma_frac"] = round(tfs / PEAK_BF16_TFLOPS, 4)
 
+    # every stage against its own roofline: algorithmic bytes (weights of the touched experts, activations
+    # in and out) and FLOPs of the step, over the stage's live event time; the bound is the larger floor
+    mfma_mult = {"router_logits": 3.0}     # W_router runs as three exact bf16 planes on the MFMAs
+    work = {
+        "pre_norm": (2 * w.T * H * 2 + H * 4, 0.0),
+        "router_logits": (w.T * H * 2 + H * w.n_experts * 4, 2.0 * w.T * H * w.n_experts),
+        "router_select": (w.T * w.n_experts * 4 + TK * 8, 0.0),
+        "permute": (TK * 4 + (w.n_experts + 1) * 4 + 2 * TK * 4, 0.0),
+        "setup": (w.T * 4, 0.0),
+        "gateup": (gu_bytes, gu_flops),
+        "down": (D * mat_bytes(H, I) + TK * I * 2 + TK * H * 2, 2.0 * TK * H * I),
+        "combine": (TK * H * 2 + w.T * H * 2 + TK * 8, 0.0),
+        "combine_norm_mix": (TK * H * 2 + 2 * w.T * H * 2 + H * 4 + TK * 8, 0.0),
+    }
+    stages_roof = {}
+    for name in stages:
+        t = stage_ms[name] / 1e3
+        if not t > 0:
+            continue
+        nbytes, nflops = work[name]
+        mflops = nflops * mfma_mult.get(name, 1.0)
+        hbm_floor = nbytes / (PEAK_HBM_GBPS * 1e9)
+        mfma_floor = mflops / (PEAK_BF16_TFLOPS * 1e12)
+        ent = {"ms": round(stage_ms[name], 4), "bytes": nbytes, "GBps": round(nbytes / t / 1e9, 1),
+               "hbm_frac": round(hbm_floor / t, 4)}
+        if nflops:
+            ent.update(flops=nflops, TFLOPs=round(nflops / t / 1e12, 2), mfma_frac=round(mfma_floor / t, 4))
+        ent["bound"] = "mfma" if mfma_floor > hbm_floor else "hbm"
+        ent["frac"] = round(max(hbm_floor, mfma_floor) / t, 4)
+        stages_roof[name] = ent
+
     res = {
         "metric": METRIC, "value": round(w.T / s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -284,6 +315,7 @@ def main():
         "routing": None if dense else {"touched_experts": D, "max_load": int(load.max()),
                                        "mean_load": TK / w.n_experts, "zero_load_experts": int((load == 0).sum())},
         "roofline": roof,
+        "stages": stages_roof,
     }
     if args.block:
         # the two norm kernels: rows read and written (plus the combine's y reads for the fused one)
