@@ -47,13 +47,14 @@ Shape shape_of(const beam_moe_config* c) {
 // Router K-split: ks parts of kc = H/ks (a multiple of the 32-wide MFMA step),
 // the fewest giving about 1024 workgroups of 128 tokens x 64 experts, each
 // part at least 4 steps long where H allows.
+constexpr int kMinSteps = 4;   // 8 or 16 made the logits kernel 40-120% slower at T = 64
 int choose_ks(const Shape& s, int T) {
   const int units = s.H / 32;
   const long tiles = (long)((T + 127) / 128) * ((s.E + 63) / 64);
   int best = 1;
   for (int ks = 1; ks <= units; ++ks) {
     if (units % ks) continue;
-    if (units / ks < 4 && best > 1) break;
+    if (units / ks < kMinSteps && best > 1) break;
     best = ks;
     if (tiles * ks >= 1024) break;
   }

@@ -152,7 +152,15 @@ __global__ __launch_bounds__(256) void router_select_kernel(int T, int E, int G,
     const float* p = partial + (size_t)t * E + tid;
     const size_t stride = (size_t)T * E;
     float z = 0.f;
-    for (int q = 0; q < ks; ++q) z += p[q * stride];
+    int q = 0;
+    for (; q + 8 <= ks; q += 8) {   // loads issued ahead of the adds, which stay in part order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p[(q + j) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z += v[j];
+    }
+    for (; q < ks; ++q) z += p[q * stride];
     if (bias) z += bias[tid];
     s_sc[tid] = 1.0f / (1.0f + expf(-z));
   }
