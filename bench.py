@@ -7,14 +7,16 @@ A step is one beam_moe_forward call (router, selection, permutation, gate/up
 GEMM + SwiGLU, down GEMM, combine) over one batch of seeded synthetic inputs
 already resident in HBM; with --block, one beam_moe_block_forward call (the
 same plus RMSNorm before, and RMSNorm + the constant-scale residual mix fused
-into the combine).  The timed region is bracketed by device
-synchronisation; per-kernel durations come from HIP events that the library
-records on its own stream between stages (beam_moe_forward_timed).
+into the combine); for the dense_* workloads, one beam_dense_mlp_forward call.
+The timed region is bracketed by device synchronisation; per-kernel durations
+come from HIP events that the library records on its own stream between
+stages (the *_timed entry points).
 
 Prints one JSON line: tokens/s (value), the whole layer's HBM GB/s and expert
 TFLOP/s with their fractions of MI355X's peaks, a roofline entry for the
-dominant kernel (gate/up), and the CPU oracle timed on a bounded sample of the
-same workload on this machine's host cores.
+dominant kernel (gate/up), every stage kernel against its own roofline
+(stages), and the CPU oracle timed on a bounded sample of the same workload
+on this machine's host cores.
 """
 from __future__ import annotations
 
