@@ -97,6 +97,28 @@ def test_tiny_skewed_bias():
     C.check_out(C.bits_of(out), ref["out"])
 
 
+ODD_SHAPES = [
+    # name, T, H, I, E, G, Gk, K, alpha, weight: smallest legal dims; no group limit with 32-row streaming
+    # tiles (K = 6); every group kept on the tiled path; fp8 on the tiled path
+    ("h128", 37, 128, 128, 16, 4, 2, 4, 1.0, "bf16"),
+    ("g1_k6", 300, 384, 256, 64, 1, 1, 6, 2.5, "bf16"),
+    ("all_groups", 700, 256, 256, 32, 8, 8, 8, 2.5, "bf16"),
+    ("fp8_tiled", 600, 256, 128, 32, 8, 4, 8, 2.5, "fp8"),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,G,Gk,K,alpha,weight", ODD_SHAPES, ids=[o[0] for o in ODD_SHAPES])
+def test_odd_shapes(name, T, H, I, E, G, Gk, K, alpha, weight):
+    w = gen.Workload("odd_" + name, 1, T, H, I, E, G, Gk, K, alpha, 0.05, 0.02, "zero", weight, 1)
+    C.say(f"[odd {name}] T={T} H={H} I={I} E={E} G={G} Gk={Gk} K={K}")
+    spec, x, wr, b = C.guarded(w, 8)
+    W, src = C.host_expert_weights(w, 8)
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    ref = oracle.forward(spec, x, wr, b, src.get)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), ref["ids"], ref["w"])
+    C.check_out(C.bits_of(out), ref["out"])
+
+
 def test_tiny_fp8_weights():
     w = gen.Workload("tiny_fp8", 1, 96, 256, 128, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", "fp8", 1)
     spec, x, wr, b = C.guarded(w, 4)
