@@ -405,6 +405,11 @@ int expert_tile_rows(const Shape& s, int T) {
   return 64;
 }
 
+// Row tiles index the grid's y dimension (at most 65535).  The streaming path
+// stays far below it: 16- and 32-row tiles only serve T*K/E <= 28, and 64-row
+// tiles at the largest T give T*K/64 + E = 33024.
+constexpr int kMaxGridY = 65535;
+
 // Largest D in {4, 2, 1}, at most cap, dividing nsteps.  (An MXFP4 scale
 // window of D dwords is then aligned: a scale row holds 4 * nsteps bytes.)
 static int pick_depth(int nsteps, int cap) {
@@ -563,6 +568,7 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
   if (use_tiled(s, T))
     return launch_gateup_tiled(s, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
                                sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+  if (max_tiles > kMaxGridY) return hipErrorInvalidConfiguration;
   const int nrows = T * s.K;
   return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
     constexpr int WT = decltype(wt)::value;
@@ -587,6 +593,7 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
                        int kparts, float* part, uint16_t* y, hipStream_t stream) {
   if (use_tiled(s, T))
     return launch_down_tiled(s, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles, y, stream);
+  if (max_tiles > kMaxGridY) return hipErrorInvalidConfiguration;
   const int nrows = T * s.K;
   return dispatch_wt_mt(s, expert_tile_rows(s, T), [&](auto wt, auto mt) {
     constexpr int WT = decltype(wt)::value;
