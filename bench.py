@@ -48,11 +48,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {"stream": ("experts.hip", "common.h"), "tiled": ("experts_tiled.hip", "common.h")}
+KERNEL_SOURCES = {"stream": ("experts.hip", "common.h"), "tiled": ("experts_tiled.hip", "common.h"),
+                  "wide": ("experts_wide.hip", "common.h")}
+KERNEL_NAMES = {"stream": "gateup_stream_kernel", "tiled": "tiled_kernel<gateup>", "wide": "wide_gateup_kernel"}
 
 
 def kernel_source_hash(kind):
-    """Hash of the sources of the gate/up kernel family ("stream" or "tiled")."""
+    """Hash of the sources of the gate/up kernel family ("stream", "tiled" or "wide")."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_top_amd", "csrc", f), "rb").read())
@@ -245,9 +247,13 @@ def main():
     s = ms / 1e3
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
-    # the library's switch to the LDS-tiled kernels (the dense path streams up to 1024 tokens)
+    # the library's gate/up kernel: LDS-tiled from 32 rows per expert (the dense path streams up to 1024
+    # tokens), and for bf16 MoE layers from 192 rows per expert the one-workgroup-per-CU kernel
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
              and w.weight != "mxfp4")
+    wide = (tiled and not dense and w.weight == "bf16" and TK >= 192 * w.n_experts and w.T * H * 2 < 2 ** 31
+            and H % 256 == 0)
+    kind = "wide" if wide else ("tiled" if tiled else "stream")
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
     gbps = gu_bytes / t_gu / 1e9
@@ -258,8 +264,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(w.name, "gateup", "tiled" if tiled else "stream")
-    roof["kernel"] = "tiled_kernel<gateup>" if tiled else "gateup_stream_kernel"
+    roof["traffic"] = load_traffic(w.name, "gateup", kind)
+    roof["kernel"] = KERNEL_NAMES[kind]
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flops_per_launch"] = gu_flops
     roof["hbm_GBps"] = round(gbps, 1)

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ sorted_pairs,
                                                     const int32_t* __restrict__ tiles,
-                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out) {
+                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
+                                                    int tile_rows) {
   using G = TiledGeom<FP8>;
   constexpr int NC = MODE == kGateUp ? 128 : kTN;        // output columns per tile
   constexpr int CST = NC * 2 + 16;                        // staged output row stride in bytes
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
   const int tile = item / NT, jn = item % NT;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int lo = offsets[e];
-  const int rows = min(offsets[e + 1] - lo - r0, kTM);
+  const int rows = min(offsets[e + 1] - lo - r0, tile_rows);   // tile_rows <= kTM (checked by the launchers)
   const int nmb = (rows + 15) / 16;
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -260,28 +261,30 @@ static int grid_for(int max_tiles, int nt) {
 
 hipError_t launch_gateup_tiled(const Shape& s, const uint16_t* x, const void* wg, const void* wu, const float* sg,
                                const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
-                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, int tile_rows, uint16_t* h,
                                hipStream_t stream) {
+  if (tile_rows < 1 || tile_rows > kTM) return hipErrorInvalidValue;
   const dim3 grid(grid_for(max_tiles, s.I / 128));
   if (s.fp8)
     hipLaunchKernelGGL((tiled_kernel<kGateUp, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
-                       offsets, sorted_pairs, tiles, ntiles, h);
+                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
   else
     hipLaunchKernelGGL((tiled_kernel<kGateUp, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
-                       offsets, sorted_pairs, tiles, ntiles, h);
+                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, const float* sd,
                              const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
-                             uint16_t* y, hipStream_t stream) {
+                             int tile_rows, uint16_t* y, hipStream_t stream) {
+  if (tile_rows < 1 || tile_rows > kTM) return hipErrorInvalidValue;
   const dim3 grid(grid_for(max_tiles, s.H / kTN));
   if (s.fp8)
     hipLaunchKernelGGL((tiled_kernel<kDown, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
-                       nullptr, offsets, nullptr, tiles, ntiles, y);
+                       nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
   else
     hipLaunchKernelGGL((tiled_kernel<kDown, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
-                       nullptr, offsets, nullptr, tiles, ntiles, y);
+                       nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
   return hipGetLastError();
 }
 
