@@ -203,6 +203,43 @@ def test_real_shape_forward(name, n_sample):
     C.say(f"[{name}] max rel {mx:.2e} mean|d|/rms {mn:.2e}")
 
 
+def test_real_shape_skew_tile_edges():
+    """Skewed routing at T = 8192: 256 rows per expert on average, so the gate/up GEMM runs one
+    workgroup per CU over 272-row tiles; the most loaded expert spans several tiles, others fall
+    just above 256 rows or hold a handful.  Ids and weights for every token; outputs for tokens at
+    row-tile edges (permuted rows 0, 255, 256, 271, 272, 543, 544 and the last of the most loaded
+    expert; the rows past 256 of an expert with 257..272; the least loaded expert's first row)."""
+    w = gen.workload("skew", 8192)
+    spec, x, wr, b = C.guarded(w, 0)
+    W = real_weights("bf16")
+    out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+    rid, rw = oracle.route(spec, x, wr, b)
+    C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
+    load = np.bincount(rid.ravel(), minlength=w.n_experts)
+    assert load.max() > 2 * 272, "the skewed draw no longer gives an expert several tiles"
+
+    def tokens_of(e):   # permuted row r of expert e is its r-th token in ascending order
+        return np.nonzero((rid == e).any(axis=1))[0]
+
+    picks = []
+    big = tokens_of(int(load.argmax()))
+    picks += [big[r] for r in (0, 255, 256, 271, 272, 543, 544) if r < len(big)] + [big[-1]]
+    near = np.nonzero((load > 256) & (load <= 272))[0]
+    if len(near):
+        t = tokens_of(int(near[0]))
+        picks += [t[256], t[-1]]
+    small = np.nonzero(load > 0)[0][np.argmin(load[load > 0])]
+    picks.append(tokens_of(int(small))[0])
+    sample = np.unique(np.array(picks))
+    src = gen.ExpertSource(w, 0)
+    src.prefetch(np.unique(rid[sample]))
+    C.say(f"[skew 8192] max load {load.max()}, oracle forward on {len(sample)} tokens")
+    ref = oracle.forward(spec, x[sample], wr, b, src.get)
+    assert np.array_equal(ref["ids"], rid[sample])
+    mx, mn = C.check_out(C.bits_of(out)[sample], ref["out"])
+    C.say(f"[skew 8192] max rel {mx:.2e} mean|d|/rms {mn:.2e}")
+
+
 def test_real_shape_max_tokens():
     """The largest T the ABI accepts, 262,144 tokens (2M (token, slot) pairs, about 8K rows per
     expert: the tiled kernels with some 29 row tiles per expert), balanced routing.  Ids and
