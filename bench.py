@@ -50,7 +50,7 @@ def log(msg):
 
 KERNEL_SOURCES = {"stream": ("experts.hip", "common.h"), "tiled": ("experts_tiled.hip", "common.h"),
                   "wide": ("experts_wide.hip", "common.h")}
-KERNEL_NAMES = {"stream": "gateup_stream_kernel", "tiled": "tiled_kernel<gateup>", "wide": "wide_gateup_kernel"}
+KERNEL_NAMES = {"stream": "gateup_stream_kernel", "tiled": "tiled_kernel<gateup>", "wide": "wide_kernel<gateup>"}
 
 
 def kernel_source_hash(kind):
@@ -248,11 +248,14 @@ def main():
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
     # the library's gate/up kernel: LDS-tiled from 32 rows per expert (the dense path streams up to 1024
-    # tokens), and for bf16 MoE layers from 192 rows per expert the one-workgroup-per-CU kernel
+    # tokens); for MoE layers the one-workgroup-per-CU kernel at 32..64 rows per expert (bf16, fp8) and
+    # from 192 (bf16)
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
              and w.weight != "mxfp4")
-    wide = (tiled and not dense and w.weight == "bf16" and TK >= 192 * w.n_experts and w.T * H * 2 < 2 ** 31
-            and H % 256 == 0)
+    wide_ok = (not dense and w.weight != "mxfp4" and TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31
+               and H % 256 == 0 and I % 256 == 0)
+    wide = wide_ok and ((TK <= 64 * w.n_experts and H % 512 == 0)
+                        or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))
     kind = "wide" if wide else ("tiled" if tiled else "stream")
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds

@@ -118,12 +118,17 @@ hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, 
                              const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                              int tile_rows, uint16_t* y, hipStream_t stream);
 
-// Prefill gate/up with one workgroup per CU and weights streamed into registers (bf16, balanced
-// expert loads): whether T selects it, its tile rows, launcher.
-bool use_wide(const Shape& s, int T);
-int wide_tile_rows();
+// Expert GEMMs with one workgroup per CU and the weights streamed into registers: which schedule T
+// selects (the balanced one runs gate/up only), its tile rows, launchers.
+enum { kWideNone = 0, kWideBalanced = 1, kWideModerate = 2 };
+int wide_schedule(const Shape& s, int T);
+int wide_tile_rows(const Shape& s, int T);
 hipError_t launch_gateup_wide(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
-                              const int32_t* offsets, const int32_t* sorted_pairs, const int32_t* tiles,
-                              const int32_t* ntiles, int max_tiles, uint16_t* h, hipStream_t stream);
+                              const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                              const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
+                              hipStream_t stream);
+hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
+                            const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                            uint16_t* y, hipStream_t stream);
 
 }  // namespace beam

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
 }
 
 int expert_tile_rows(const Shape& s, int T) {
-  if (use_wide(s, T)) return wide_tile_rows();
+  if (wide_schedule(s, T) != kWideNone) return wide_tile_rows(s, T);
   if (use_tiled(s, T)) return tiled_tile_rows();
   const long mean = ((long)T * s.K + s.E - 1) / s.E;
   if (mean <= 12) return 16;
@@ -566,8 +566,9 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
                          const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, int kparts, float* part,
                          uint16_t* h, hipStream_t stream) {
-  if (use_wide(s, T))
-    return launch_gateup_wide(s, T, x, wg, wu, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+  if (wide_schedule(s, T) != kWideNone)
+    return launch_gateup_wide(s, T, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
+                              sorted_pairs, tiles, ntiles, max_tiles, h, stream);
   if (use_tiled(s, T))
     return launch_gateup_tiled(s, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
                                sorted_pairs, tiles, ntiles, max_tiles, expert_tile_rows(s, T), h, stream);
@@ -594,6 +595,8 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part, uint16_t* y, hipStream_t stream) {
+  if (wide_schedule(s, T) == kWideModerate)
+    return launch_down_wide(s, T, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles, y, stream);
   if (use_tiled(s, T))
     return launch_down_tiled(s, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles,
                              expert_tile_rows(s, T), y, stream);
