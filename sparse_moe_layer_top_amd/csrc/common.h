@@ -64,6 +64,11 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t q, float scale) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// E8M0 block scale byte -> float 2^(e-127) (codes 1..254; 0 gives 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ---- workspace carve-up (host) ----
@@ -124,10 +129,10 @@ enum { kWideNone = 0, kWideBalanced = 1, kWideModerate = 2 };
 int wide_schedule(const Shape& s, int T);
 int wide_tile_rows(const Shape& s, int T);
 hipError_t launch_gateup_wide(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
-                              const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                              const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                               hipStream_t stream);
-hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
+hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                             uint16_t* y, hipStream_t stream);
 

@@ -59,11 +59,6 @@ struct WFrag<kWMX> {
   static __device__ __forceinline__ bf16x8 frag(u32x4 v, int a, float scale) { return e2m1x8_to_bf16x8(v[a], scale); }
 };
 
-// E8M0 block scale byte -> float 2^(e-127) (codes 1..254; 0 gives 2^-127)
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e ? (e << 23) : 0x00400000u);
-}
-
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -567,8 +562,7 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
                          const int32_t* tiles, const int32_t* ntiles, int max_tiles, int kparts, float* part,
                          uint16_t* h, hipStream_t stream) {
   if (wide_schedule(s, T) != kWideNone)
-    return launch_gateup_wide(s, T, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
-                              sorted_pairs, tiles, ntiles, max_tiles, h, stream);
+    return launch_gateup_wide(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, max_tiles, h, stream);
   if (use_tiled(s, T))
     return launch_gateup_tiled(s, x, wg, wu, static_cast<const float*>(sg), static_cast<const float*>(su), offsets,
                                sorted_pairs, tiles, ntiles, max_tiles, expert_tile_rows(s, T), h, stream);
@@ -596,7 +590,7 @@ hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part, uint16_t* y, hipStream_t stream) {
   if (wide_schedule(s, T) == kWideModerate)
-    return launch_down_wide(s, T, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles, y, stream);
+    return launch_down_wide(s, T, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
   if (use_tiled(s, T))
     return launch_down_tiled(s, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles,
                              expert_tile_rows(s, T), y, stream);

@@ -68,14 +68,15 @@ constexpr int kWBalancedMT = 17;             // 272-row tiles: a whole balanced 
 constexpr int kWModerateMT = 6;              // 96-row tiles: up to 64 rows per expert on average
 
 enum { kWGateUp = 0, kWDown = 1 };
+enum { kWtBF16 = 0, kWtFP8 = 1 };
 
-template <bool FP8, int MODE, int MT, int NB>
+template <int WT, int MODE, int MT, int NB>
 struct WideCfg {
-  static constexpr int EB = FP8 ? 1 : 2;                      // weight bytes per element
+  static constexpr int WIN_BYTES = WT == kWtBF16 ? 128 : 64;  // weight bytes per row per window
   static constexpr int ROWS = 16 * MT;
   static constexpr int GROUPS = 2 * MT;                       // 8-row activation load groups per window
   static constexpr int GPW = (GROUPS + kWWaves - 1) / kWWaves;
-  static constexpr int WLD = FP8 ? 1 : 2;                     // 16-byte weight loads per block per window
+  static constexpr int WLD = WT == kWtBF16 ? 2 : 1;           // 16-byte weight loads per block per window
   static constexpr int COLS = MODE == kWGateUp ? kWWaves * 8 * NB : kWWaves * 16 * NB;   // output columns
   static constexpr int CST = COLS * 2 + 16;                   // staged output row stride, bytes
   static constexpr int OUT_ROWS = (ROWS + kWRing - 1) / kWRing;   // output rows staged per stage
@@ -101,17 +102,17 @@ __device__ __forceinline__ void stage_fill(uint8_t* st, __amdgpu_buffer_rsrc_t r
 
 // (The weight pointers are not restrict: with them the compiler moves each window's weight loads
 // down to their first use, three windows later, which empties the pipeline.)
-template <bool FP8, int MODE, int MT, int NB>
+template <int WT, int MODE, int MT, int NB>
 __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const uint16_t* __restrict__ act,
-                                                   const void* w0, const void* w1, const float* __restrict__ s0,
-                                                   const float* __restrict__ s1,
+                                                   const void* w0, const void* w1, const void* s0, const void* s1,
                                                    const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ sorted_pairs,
                                                    const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
                                                    long act_bytes) {
-  using C = WideCfg<FP8, MODE, MT, NB>;
+  using C = WideCfg<WT, MODE, MT, NB>;
   constexpr int GPW = C::GPW;
+  constexpr bool FP8 = WT == kWtFP8;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::STAGE];
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   // This wave's weight rows through buffer resources over the expert's matrices: gate/up, rows
   // c, c + 16, ... of both matrices (c the wave's first intermediate column); down, NB consecutive
   // blocks of 16 rows.  Block n is 16n rows past the first (soffset).
-  const size_t wmat = (size_t)(MODE == kWGateUp ? I : H) * KD * C::EB;   // bytes per expert matrix
+  const int rowb = KD / kWWin * C::WIN_BYTES;                             // bytes per weight row
+  const size_t wmat = (size_t)(MODE == kWGateUp ? I : H) * rowb;          // bytes per expert matrix
   const __amdgpu_buffer_rsrc_t wr0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(static_cast<const uint8_t*>(w0) + e * wmat), (short)0, (int)wmat, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t wr1 =
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                        : wr0;
   constexpr int WCOLS = MODE == kWGateUp ? 8 * NB : 16 * NB;   // this wave's output columns
   const int wc0 = jn * C::COLS + wave * WCOLS;
-  const uint32_t woff = ((uint32_t)(wc0 + l16) * KD + 16 * q) * C::EB;
-  const int bstride = 16 * KD * C::EB;   // bytes between blocks of 16 weight rows
+  const uint32_t woff = (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
+  const int bstride = 16 * rowb;         // bytes between blocks of 16 weight rows
   // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB groups)
   int roff[2];
 #pragma unroll
@@ -205,16 +207,17 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     constexpr int S = decltype(sc)::value;
     stage_fill(stage(sc), arsrc, aslot, aoff, GPW, win * kWWin * 2);
     constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
+    const int wsoff = win * C::WIN_BYTES;
 #pragma unroll
     for (int j = 0; j < C::WLD; ++j) {
 #pragma unroll
       for (int n = 0; n < NW0; ++n)
         wb[S][j][n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, win * kWWin * C::EB + 16 * j + n * bstride, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, wsoff + 16 * j + n * bstride, 0));
 #pragma unroll
       for (int n = NW0; n < NB; ++n)
-        wb[S][j][n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    wr1, woff, win * kWWin * C::EB + 16 * j + (n - NW0) * bstride, 0));
+        wb[S][j][n] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr1, woff, wsoff + 16 * j + (n - NW0) * bstride, 0));
     }
   };
   auto compute = [&](auto sc) {
@@ -306,8 +309,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 #pragma unroll
     for (int n = 0; n < NB / 2; ++n) {
       const int c = wave * WCOLS + n * 16 + l16;   // column within the tile
-      const float sg = FP8 ? s0[(size_t)e * I + jn * C::COLS + c] : 1.f;
-      const float su = FP8 ? s1[(size_t)e * I + jn * C::COLS + c] : 1.f;
+      const float sg = FP8 ? static_cast<const float*>(s0)[(size_t)e * I + jn * C::COLS + c] : 1.f;
+      const float su = FP8 ? static_cast<const float*>(s1)[(size_t)e * I + jn * C::COLS + c] : 1.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < nmb) {
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int c = wave * WCOLS + n * 16 + l16;
-      const float sd = FP8 ? s0[(size_t)e * H + jn * C::COLS + c] : 1.f;
+      const float sd = FP8 ? static_cast<const float*>(s0)[(size_t)e * H + jn * C::COLS + c] : 1.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m < nmb) {
@@ -352,21 +355,23 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 //   * balanced bf16 (at least 192 rows per expert on average): the gate/up GEMM, 272-row tiles
 //     (the LDS-tiled kernel, which skips empty row blocks, does as well below that); down stays on
 //     the LDS-tiled kernel over the same tiles;
-//   * 32 to 64 rows per expert on average (bf16 or fp8): both GEMMs, 96-row tiles.
+//   * 32 to 64 rows per expert on average (bf16 or fp8): both GEMMs, 96-row tiles.  (MXFP4 stays on
+//     the streaming kernels: with 8 code bytes and a scale byte per lane and window this schedule
+//     ran slower than they do, 2.97 against 2.77 ms on 2048 tokens.)
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
 // and the token rows must fit one buffer resource (byte offsets below 2^31).
 static int wide_mode(const Shape& s, int T) {
-  if (s.mx || s.dense) return kWideNone;
+  if (s.dense || s.mx) return kWideNone;
   const long tk = (long)T * s.K;
   if (tk < 32L * s.E) return kWideNone;
   if ((long)T * s.H * 2 >= (1L << 31)) return kWideNone;
   if (s.H % (kWWin * kWRing) != 0 || s.I % (kWWin * kWRing) != 0) return kWideNone;
   if (tk <= 64L * s.E)
-    return s.I % WideCfg<false, kWGateUp, kWModerateMT, 4>::COLS == 0 &&
-                   s.H % WideCfg<false, kWDown, kWModerateMT, 4>::COLS == 0
+    return s.I % WideCfg<kWtBF16, kWGateUp, kWModerateMT, 4>::COLS == 0 &&
+                   s.H % WideCfg<kWtBF16, kWDown, kWModerateMT, 4>::COLS == 0
                ? kWideModerate
                : kWideNone;
-  if (!s.fp8 && tk >= 192L * s.E && s.I % WideCfg<false, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
+  if (!s.fp8 && tk >= 192L * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
       use_tiled(s, T))
     return kWideBalanced;
   return kWideNone;
@@ -378,47 +383,47 @@ int wide_tile_rows(const Shape& s, int T) {
   return wide_mode(s, T) == kWideBalanced ? 16 * kWBalancedMT : 16 * kWModerateMT;
 }
 
-template <bool FP8, int MODE, int MT, int NB>
+template <int WT, int MODE, int MT, int NB>
 static hipError_t wide_launch(const Shape& s, int T, const uint16_t* act, const void* w0, const void* w1,
-                              const float* s0, const float* s1, const int32_t* offsets, const int32_t* sorted_pairs,
+                              const void* s0, const void* s1, const int32_t* offsets, const int32_t* sorted_pairs,
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* out,
                               hipStream_t stream) {
-  using C = WideCfg<FP8, MODE, MT, NB>;
+  using C = WideCfg<WT, MODE, MT, NB>;
   const long items = (long)max_tiles * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
   const int grid = (int)((items + kWXcds - 1) / kWXcds * kWXcds);
-  hipLaunchKernelGGL((wide_kernel<FP8, MODE, MT, NB>), dim3(grid), dim3(kWWaves * kWave), 0, stream, s.H, s.I, s.K,
+  hipLaunchKernelGGL((wide_kernel<WT, MODE, MT, NB>), dim3(grid), dim3(kWWaves * kWave), 0, stream, s.H, s.I, s.K,
                      act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_wide(const Shape& s, int T, const uint16_t* x, const void* wg, const void* wu,
-                              const float* sg, const float* su, const int32_t* offsets, const int32_t* sorted_pairs,
+                              const void* sg, const void* su, const int32_t* offsets, const int32_t* sorted_pairs,
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* h,
                               hipStream_t stream) {
   switch (wide_mode(s, T)) {
     case kWideBalanced:
-      return wide_launch<false, kWGateUp, kWBalancedMT, 2>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
-                                                           ntiles, max_tiles, h, stream);
+      return wide_launch<kWtBF16, kWGateUp, kWBalancedMT, 2>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
+                                                             ntiles, max_tiles, h, stream);
     case kWideModerate:
       if (s.fp8)
-        return wide_launch<true, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
-                                                            ntiles, max_tiles, h, stream);
-      return wide_launch<false, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
-                                                           ntiles, max_tiles, h, stream);
+        return wide_launch<kWtFP8, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
+                                                              ntiles, max_tiles, h, stream);
+      return wide_launch<kWtBF16, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
+                                                             ntiles, max_tiles, h, stream);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const float* sd,
+hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                             uint16_t* y, hipStream_t stream) {
   if (wide_mode(s, T) != kWideModerate) return hipErrorInvalidValue;
   if (s.fp8)
-    return wide_launch<true, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
-                                                      ntiles, max_tiles, y, stream);
-  return wide_launch<false, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
-                                                     ntiles, max_tiles, y, stream);
+    return wide_launch<kWtFP8, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
+                                                        ntiles, max_tiles, y, stream);
+  return wide_launch<kWtBF16, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
+                                                       ntiles, max_tiles, y, stream);
 }
 
 }  // namespace beam
