@@ -9,6 +9,8 @@
 //   y = bf16( h Wd^T )                        down
 // FP8 (OCP e4m3) weights convert exactly to bf16 in registers; the
 // per-output-channel scale multiplies the fp32 accumulator in the epilogue.
+// MXFP4 weights (E2M1 codes, one E8M0 scale per 32 inputs) convert with their
+// block scale to bf16 in registers, exactly.
 //
 // A workgroup takes one row tile of an expert (MT blocks of 16 rows) and a
 // block of output columns.  What sets the streaming rate of a CU is the bytes
@@ -32,6 +34,11 @@
 //   * Lane (r = l%16, q = l/16) of MFMA half a of a window uses k in
 //     [16q + 8a, +8) of the window for both operands (fp8: the lane's 16
 //     weight bytes are k [16q, 16q + 16), half a the a-th 8 of them).
+//     MXFP4 windows are 128 deep: lane q's 16 code bytes are k [32q, +32),
+//     one scale block, and MFMA slice t uses k [32q + 8t, +8); the
+//     activations sit as two 64-deep halves, so the lane reads half q/2,
+//     chunk 4(q%2) + t (every lane group of a ds_read_b128 shares q, so the
+//     swizzle keeps it conflict-free).
 //   * Every row block runs every window (rows past the tile's end hold its
 //     last row, zeros or stale values, and are never stored: an MFMA output
 //     row depends on its own A row only), so the compute has no branches and
@@ -68,10 +75,12 @@ constexpr int kWBalancedMT = 17;             // 272-row tiles: a whole balanced 
 constexpr int kWModerateMT = 6;              // 96-row tiles: up to 64 rows per expert on average
 
 enum { kWGateUp = 0, kWDown = 1 };
-enum { kWtBF16 = 0, kWtFP8 = 1 };
+enum { kWtBF16 = 0, kWtFP8 = 1, kWtMX = 2 };
 
 template <int WT, int MODE, int MT, int NB>
 struct WideCfg {
+  static constexpr int WIN_K = WT == kWtMX ? 128 : 64;         // k per window
+  static constexpr int HALVES = WIN_K / 64;                   // 64-deep activation halves per window
   static constexpr int WIN_BYTES = WT == kWtBF16 ? 128 : 64;  // weight bytes per row per window
   static constexpr int ROWS = 16 * MT;
   static constexpr int GROUPS = 2 * MT;                       // 8-row activation load groups per window
@@ -80,7 +89,8 @@ struct WideCfg {
   static constexpr int COLS = MODE == kWGateUp ? kWWaves * 8 * NB : kWWaves * 16 * NB;   // output columns
   static constexpr int CST = COLS * 2 + 16;                   // staged output row stride, bytes
   static constexpr int OUT_ROWS = (ROWS + kWRing - 1) / kWRing;   // output rows staged per stage
-  static constexpr int A_BYTES = (GROUPS + 1) * 1024;         // + one spare slot
+  static constexpr int SUB = (GROUPS + 1) * 1024;             // a 64-deep half + one spare slot
+  static constexpr int A_BYTES = HALVES * SUB;
   static constexpr int STAGE = ((A_BYTES > OUT_ROWS * CST ? A_BYTES : OUT_ROWS * CST) + 1023) / 1024 * 1024;
   static_assert(kWRing * STAGE <= 160 * 1024, "LDS");
   static_assert(MODE == kWDown || NB % 2 == 0, "gate/up blocks come in pairs");
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                                                    long act_bytes) {
   using C = WideCfg<WT, MODE, MT, NB>;
   constexpr int GPW = C::GPW;
-  constexpr bool FP8 = WT == kWtFP8;
+  constexpr bool FP8 = WT == kWtFP8, MX = WT == kWtMX;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[C::STAGE];
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   // This wave's weight rows through buffer resources over the expert's matrices: gate/up, rows
   // c, c + 16, ... of both matrices (c the wave's first intermediate column); down, NB consecutive
   // blocks of 16 rows.  Block n is 16n rows past the first (soffset).
-  const int rowb = KD / kWWin * C::WIN_BYTES;                             // bytes per weight row
+  const int rowb = KD / C::WIN_K * C::WIN_BYTES;                          // bytes per weight row
   const size_t wmat = (size_t)(MODE == kWGateUp ? I : H) * rowb;          // bytes per expert matrix
   const __amdgpu_buffer_rsrc_t wr0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(static_cast<const uint8_t*>(w0) + e * wmat), (short)0, (int)wmat, kRsrcWord3);
@@ -178,9 +188,27 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   const uint32_t woff = (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
   const int bstride = 16 * rowb;         // bytes between blocks of 16 weight rows
   // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB groups)
-  int roff[2];
+  // (MXFP4: chunk 4(q%2) + t of the lane's half q/2, t = 0..3)
+  constexpr int NSL = MX ? 4 : 2;   // MFMA slices per window
+  int roff[NSL];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) roff[a] = (l16 / 8) * 1024 + ((l16 % 8) * 8 + ((2 * q + a) ^ (l16 % 8) ^ (l16 / 8))) * 16;
+  for (int t = 0; t < NSL; ++t) {
+    const int c = MX ? 4 * (q % 2) + t : 2 * q + t;
+    roff[t] = (MX ? (q / 2) * C::SUB : 0) + (l16 / 8) * 1024 + ((l16 % 8) * 8 + (c ^ (l16 % 8) ^ (l16 / 8))) * 16;
+  }
+  // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword, the lane's is byte q
+  const int srowb = KD / 32;
+  const size_t smat = (size_t)(MODE == kWGateUp ? I : H) * srowb;
+  const __amdgpu_buffer_rsrc_t sr0 =
+      MX ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s0) + e * smat),
+                                             (short)0, (int)smat, kRsrcWord3)
+         : wr0;
+  const __amdgpu_buffer_rsrc_t sr1 =
+      MX && MODE == kWGateUp
+          ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s1) + e * smat),
+                                              (short)0, (int)smat, kRsrcWord3)
+          : sr0;
+  const uint32_t soff = (uint32_t)(wc0 + l16) * srowb;
 
   // Stage accesses name the stage arrays themselves: the compiler gives each LDS variable its own
   // alias scope, which lets it match a read of a stage to the direct-to-LDS loads into that stage (and
@@ -189,24 +217,36 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   auto stage_probe = [&](const uint8_t* st) -> uint32_t {
     uint32_t v = 0;
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) v |= *reinterpret_cast<const uint32_t*>(st + aslot[i] + lane * 16);
+    for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) v |= *reinterpret_cast<const uint32_t*>(st + h * C::SUB + aslot[i] + lane * 16);
     return v;
   };
 
   u32x4 wb[kWRing][C::WLD][NB];   // [slot][16-byte load][block]; gate/up blocks: NB/2 gate then NB/2 up
+  uint32_t wsc[kWRing][MX ? NB : 1];   // MXFP4 scale dwords
   f32x4 acc[MT][NB];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nwin = KD / kWWin;   // a multiple of kWRing (checked by the launcher)
+  const int nwin = KD / C::WIN_K;   // a multiple of kWRing (checked by the launcher)
   // Window win into ring slot S.  Past the end the last window is issued again (into a slot nothing
   // reads): every round issues the same loads.
   auto issue = [&](auto sc, int win) {
     constexpr int S = decltype(sc)::value;
-    stage_fill(stage(sc), arsrc, aslot, aoff, GPW, win * kWWin * 2);
+#pragma unroll
+    for (int h = 0; h < C::HALVES; ++h)
+      stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
     constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
+    if constexpr (MX) {
+#pragma unroll
+      for (int n = 0; n < NW0; ++n) wsc[S][n] = __builtin_amdgcn_raw_buffer_load_b32(sr0, soff, 4 * win + n * 16 * srowb, 0);
+#pragma unroll
+      for (int n = NW0; n < NB; ++n)
+        wsc[S][n] = __builtin_amdgcn_raw_buffer_load_b32(sr1, soff, 4 * win + (n - NW0) * 16 * srowb, 0);
+    }
     const int wsoff = win * C::WIN_BYTES;
 #pragma unroll
     for (int j = 0; j < C::WLD; ++j) {
@@ -223,12 +263,19 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   auto compute = [&](auto sc) {
     constexpr int S = decltype(sc)::value;
     const uint8_t* st = stage(sc);
+    float msc[MX ? NB : 1];
+    if constexpr (MX) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+      for (int n = 0; n < NB; ++n) msc[n] = e8m0_to_f32((wsc[S][n] >> (8 * q)) & 0xFFu);
+    }
+#pragma unroll
+    for (int a = 0; a < NSL; ++a) {
       bf16x8 b[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        if constexpr (FP8) {
+        if constexpr (MX) {
+          b[n] = e2m1x8_to_bf16x8(wb[S][0][n][a], msc[n]);
+        } else if constexpr (FP8) {
           const u32x4 v = wb[S][0][n];
           b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{v[0], v[1]} : u32x2{v[2], v[3]});
         } else {
@@ -243,7 +290,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
       }
     }
     constexpr int kAhead = MT < 3 ? MT : 3;
-    constexpr int kReads = 2 * MT;
+    constexpr int kReads = NSL * MT;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
 #pragma unroll
     for (int i = 0; i < kReads - kAhead; ++i) {
@@ -355,23 +402,22 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 //   * balanced bf16 (at least 192 rows per expert on average): the gate/up GEMM, 272-row tiles
 //     (the LDS-tiled kernel, which skips empty row blocks, does as well below that); down stays on
 //     the LDS-tiled kernel over the same tiles;
-//   * 32 to 64 rows per expert on average (bf16 or fp8): both GEMMs, 96-row tiles.  (MXFP4 stays on
-//     the streaming kernels: with 8 code bytes and a scale byte per lane and window this schedule
-//     ran slower than they do, 2.97 against 2.77 ms on 2048 tokens.)
+//   * 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row tiles.
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
 // and the token rows must fit one buffer resource (byte offsets below 2^31).
 static int wide_mode(const Shape& s, int T) {
-  if (s.dense || s.mx) return kWideNone;
+  if (s.dense) return kWideNone;
   const long tk = (long)T * s.K;
   if (tk < 32L * s.E) return kWideNone;
   if ((long)T * s.H * 2 >= (1L << 31)) return kWideNone;
-  if (s.H % (kWWin * kWRing) != 0 || s.I % (kWWin * kWRing) != 0) return kWideNone;
+  const int wk = s.mx ? 128 : kWWin;   // k per window
+  if (s.H % (wk * kWRing) != 0 || s.I % (wk * kWRing) != 0) return kWideNone;
   if (tk <= 64L * s.E)
     return s.I % WideCfg<kWtBF16, kWGateUp, kWModerateMT, 4>::COLS == 0 &&
                    s.H % WideCfg<kWtBF16, kWDown, kWModerateMT, 4>::COLS == 0
                ? kWideModerate
                : kWideNone;
-  if (!s.fp8 && tk >= 192L * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
+  if (!s.fp8 && !s.mx && tk >= 192L * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
       use_tiled(s, T))
     return kWideBalanced;
   return kWideNone;
@@ -405,6 +451,9 @@ hipError_t launch_gateup_wide(const Shape& s, int T, const uint16_t* x, const vo
       return wide_launch<kWtBF16, kWGateUp, kWBalancedMT, 2>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
                                                              ntiles, max_tiles, h, stream);
     case kWideModerate:
+      if (s.mx)
+        return wide_launch<kWtMX, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
+                                                             ntiles, max_tiles, h, stream);
       if (s.fp8)
         return wide_launch<kWtFP8, kWGateUp, kWModerateMT, 4>(s, T, x, wg, wu, sg, su, offsets, sorted_pairs, tiles,
                                                               ntiles, max_tiles, h, stream);
@@ -419,6 +468,9 @@ hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void
                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                             uint16_t* y, hipStream_t stream) {
   if (wide_mode(s, T) != kWideModerate) return hipErrorInvalidValue;
+  if (s.mx)
+    return wide_launch<kWtMX, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
+                                                       ntiles, max_tiles, y, stream);
   if (s.fp8)
     return wide_launch<kWtFP8, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
                                                         ntiles, max_tiles, y, stream);
