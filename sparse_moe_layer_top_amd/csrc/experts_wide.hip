@@ -196,7 +196,10 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     const int c = MX ? 4 * (q % 2) + t : 2 * q + t;
     roff[t] = (MX ? (q / 2) * C::SUB : 0) + (l16 / 8) * 1024 + ((l16 % 8) * 8 + (c ^ (l16 % 8) ^ (l16 / 8))) * 16;
   }
-  // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword, the lane's is byte q
+  // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword (the lane's block
+  // is byte q), a round of the ring's four windows one 16-byte load.  Each row's scale bytes are read
+  // once per round, not once per window: with a line's worth of rows per workgroup in flight, lines
+  // fetched for one window do not reliably stay cached until the next.
   const int srowb = KD / 32;
   const size_t smat = (size_t)(MODE == kWGateUp ? I : H) * srowb;
   const __amdgpu_buffer_rsrc_t sr0 =
@@ -224,7 +227,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   };
 
   u32x4 wb[kWRing][C::WLD][NB];   // [slot][16-byte load][block]; gate/up blocks: NB/2 gate then NB/2 up
-  uint32_t wsc[kWRing][MX ? NB : 1];   // MXFP4 scale dwords
+  u32x4 wsc[MX ? NB : 1];    // MXFP4 scale dwords of a round's four windows (loaded with ring slot 0)
+  u32x4 wsck[MX ? NB : 1];   // the same, kept through the round while the next round's are in flight
   f32x4 acc[MT][NB];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -240,12 +244,15 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     for (int h = 0; h < C::HALVES; ++h)
       stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
     constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
-    if constexpr (MX) {
+    if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
+      const int rsoff = 16 * (win / kWRing);
 #pragma unroll
-      for (int n = 0; n < NW0; ++n) wsc[S][n] = __builtin_amdgcn_raw_buffer_load_b32(sr0, soff, 4 * win + n * 16 * srowb, 0);
+      for (int n = 0; n < NW0; ++n)
+        wsc[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr0, soff, rsoff + n * 16 * srowb, 0));
 #pragma unroll
       for (int n = NW0; n < NB; ++n)
-        wsc[S][n] = __builtin_amdgcn_raw_buffer_load_b32(sr1, soff, 4 * win + (n - NW0) * 16 * srowb, 0);
+        wsc[n] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr1, soff, rsoff + (n - NW0) * 16 * srowb, 0));
     }
     const int wsoff = win * C::WIN_BYTES;
 #pragma unroll
@@ -266,7 +273,10 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     float msc[MX ? NB : 1];
     if constexpr (MX) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) msc[n] = e8m0_to_f32((wsc[S][n] >> (8 * q)) & 0xFFu);
+      for (int n = 0; n < NB; ++n) {
+        if constexpr (S == 0) wsck[n] = wsc[n];   // the next issue into slot 0 reloads wsc
+        msc[n] = e8m0_to_f32((wsck[n][S] >> (8 * q)) & 0xFFu);
+      }
     }
 #pragma unroll
     for (int a = 0; a < NSL; ++a) {
