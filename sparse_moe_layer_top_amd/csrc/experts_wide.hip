@@ -243,6 +243,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 #pragma unroll
     for (int h = 0; h < C::HALVES; ++h)
       stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
+    __builtin_amdgcn_sched_barrier(0);   // a fixed load order in every issue
     constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
     if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
       const int rsoff = 16 * (win / kWRing);
@@ -327,12 +328,17 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Each round enters with windows w .. w+2 in flight, issued in the same order on both paths into
+  // the loop (prologue and back edge), so the compiler's view of the pending loads at the loop's head
+  // is exact and its waits stay precise.
   issue(std::integral_constant<int, 0>{}, 0);
+  __builtin_amdgcn_sched_barrier(0);
   issue(std::integral_constant<int, 1>{}, 1);
+  __builtin_amdgcn_sched_barrier(0);
   issue(std::integral_constant<int, 2>{}, 2);
   __builtin_amdgcn_sched_barrier(0);
-  open(std::integral_constant<int, 0>{}, 0);
-  for (int w = 0;; w += kWRing) {   // each round enters after window w's opening
+  for (int w = 0; w < nwin; w += kWRing) {
+    open(std::integral_constant<int, 0>{}, w);
     run(std::integral_constant<int, 0>{});
     open(std::integral_constant<int, 1>{}, w + 1);
     run(std::integral_constant<int, 1>{});
@@ -340,8 +346,6 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     run(std::integral_constant<int, 2>{});
     open(std::integral_constant<int, 3>{}, w + 3);
     run(std::integral_constant<int, 3>{});
-    if (w + kWRing >= nwin) break;
-    open(std::integral_constant<int, 0>{}, w + kWRing);
   }
 
   // Epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block.  Stage the bf16 output
