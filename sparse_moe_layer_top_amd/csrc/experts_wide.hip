@@ -1,6 +1,6 @@
 // Grouped expert GEMMs with one workgroup per CU and the weights streamed
 // straight into registers: the prefill gate/up for balanced bf16 layers, and
-// both GEMMs (bf16 or fp8 weights) at a few dozen rows per expert.
+// both GEMMs (bf16, fp8 or MXFP4 weights) at a few dozen rows per expert.
 //
 // Same arithmetic as the other expert kernels (each expert a SwiGLU MLP,
 // Reflection Beam 1.0 overview, section "Mixture of Experts"; the SwiGLU
@@ -38,7 +38,8 @@
 //     one scale block, and MFMA slice t uses k [32q + 8t, +8); the
 //     activations sit as two 64-deep halves, so the lane reads half q/2,
 //     chunk 4(q%2) + t (every lane group of a ds_read_b128 shares q, so the
-//     swizzle keeps it conflict-free).
+//     swizzle keeps it conflict-free).  A row's scale bytes for the ring's
+//     four windows arrive as one 16-byte load with ring slot 0.
 //   * Every row block runs every window (rows past the tile's end hold its
 //     last row, zeros or stale values, and are never stored: an MFMA output
 //     row depends on its own A row only), so the compute has no branches and
@@ -57,7 +58,8 @@
 //
 // Balanced bf16 gate/up (272-row tiles, NB = 2): the MFMAs of a window read
 // one activation fragment per two MFMAs from LDS, which bounds the compute
-// phase at about 70% of the MFMA rate; the loads overlap it only in part.
+// phase at about 65% of the MFMA rate (measured for that mix alone); the
+// loads overlap it only in part.
 // At 96-row tiles (NB = 4) the work is HBM-bound: a window brings 12 KB of
 // activations and 64 KB (bf16) of weights per CU.
 #include <type_traits>
