@@ -102,6 +102,7 @@ ODD_SHAPES = [
     # tiles (K = 6); every group kept (LDS-tiled GEMMs); fp8 on the LDS-tiled path; the
     # one-workgroup-per-CU gate/up (375 rows per expert on average: 272-row tiles, tall and short);
     # both one-workgroup-per-CU GEMMs at about 60 rows per expert (96-row tiles), bf16, fp8 and MXFP4
+    # (MXFP4 also over two rounds of the four-window ring, whose scale bytes arrive one load per round)
     ("h128", 37, 128, 128, 16, 4, 2, 4, 1.0, "bf16"),
     ("g1_k6", 300, 384, 256, 64, 1, 1, 6, 2.5, "bf16"),
     ("all_groups", 700, 256, 256, 32, 8, 8, 8, 2.5, "bf16"),
@@ -110,6 +111,7 @@ ODD_SHAPES = [
     ("moderate_bf16", 250, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
     ("moderate_fp8", 240, 512, 256, 32, 8, 4, 8, 2.5, "fp8"),
     ("moderate_mx", 230, 512, 512, 32, 8, 4, 8, 2.5, "mxfp4"),
+    ("moderate_mx_2rounds", 220, 1024, 1024, 32, 8, 4, 8, 2.5, "mxfp4"),
 ]
 
 
