@@ -248,14 +248,14 @@ def main():
     hbm_gbps = layer_bytes / s / 1e9
     tflops = layer_flops / s / 1e12
     # the library's gate/up kernel: LDS-tiled from 32 rows per expert (the dense path streams up to 1024
-    # tokens); for MoE layers the one-workgroup-per-CU kernel at 32..64 rows per expert (any weight type)
-    # and from 192 (bf16)
+    # tokens); the one-workgroup-per-CU kernel for MoE layers at 32..64 rows per expert (any weight
+    # type), and from 192 rows per expert (bf16) wherever the LDS-tiled one would run, dense included
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
              and w.weight != "mxfp4")
     wk = 128 if w.weight == "mxfp4" else 64      # k per window
-    wide_ok = (not dense and TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31
+    wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31
                and H % (4 * wk) == 0 and I % (4 * wk) == 0)
-    wide = wide_ok and ((TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
+    wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
                         or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))
     kind = "wide" if wide else ("tiled" if tiled else "stream")
     t_gu = stage_ms["gateup"] / 1e3

@@ -75,6 +75,7 @@ constexpr int kWWaves = 8;
 constexpr int kWXcds = 8;
 constexpr int kWBalancedMT = 17;             // 272-row tiles: a whole balanced expert
 constexpr int kWModerateMT = 6;              // 96-row tiles: up to 64 rows per expert on average
+constexpr int kWDenseTileGroup = 4;          // dense layers: row tiles per group of the work order
 
 enum { kWGateUp = 0, kWDown = 1 };
 enum { kWtBF16 = 0, kWtFP8 = 1, kWtMX = 2 };
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                                                    const int32_t* __restrict__ sorted_pairs,
                                                    const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
-                                                   long act_bytes) {
+                                                   long act_bytes, int tgroup) {
   using C = WideCfg<WT, MODE, MT, NB>;
   constexpr int GPW = C::GPW;
   constexpr bool FP8 = WT == kWtFP8, MX = WT == kWtMX;
@@ -139,13 +140,17 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 
   const int KD = MODE == kWGateUp ? H : I;                  // reduction length
   const int NT = (MODE == kWGateUp ? I : H) / C::COLS;      // column blocks per tile
-  const int nitems = ntiles[0] * NT;
+  // Work items in groups of tgroup row tiles, column block outer and tile inner within a group (the
+  // last group padded; tgroup = 1: one tile's column blocks after another).
+  const int nitems = (ntiles[0] + tgroup - 1) / tgroup * tgroup * NT;
   const int per_xcd = (nitems + kWXcds - 1) / kWXcds;
   const int slot = blockIdx.x / kWXcds;
   if (slot >= per_xcd) return;
   const int item = (blockIdx.x % kWXcds) * per_xcd + slot;
   if (item >= nitems) return;
-  const int tile = item / NT, jn = item % NT;
+  const int grp = item / (tgroup * NT), rr = item % (tgroup * NT);
+  const int tile = grp * tgroup + rr % tgroup, jn = rr / tgroup;
+  if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int lo = offsets[e];
   const int rows = min(offsets[e + 1] - lo - r0, C::ROWS);
@@ -413,23 +418,22 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   }
 }
 
-// Which one-workgroup-per-CU schedule, if any, a layer takes (MoE layers only; the dense path keeps
-// the streaming and LDS-tiled kernels):
-//   * balanced bf16 (at least 192 rows per expert on average): the gate/up GEMM, 272-row tiles
-//     (the LDS-tiled kernel, which skips empty row blocks, does as well below that); down stays on
-//     the LDS-tiled kernel over the same tiles;
-//   * 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row tiles.
+// Which one-workgroup-per-CU schedule, if any, a layer takes:
+//   * balanced bf16 (at least 192 rows per expert on average, or a dense layer on the LDS-tiled
+//     path): the gate/up GEMM, 272-row tiles (the LDS-tiled kernel, which skips empty row blocks,
+//     does as well below that); down stays on the LDS-tiled kernel over the same tiles;
+//   * MoE layers with 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row
+//     tiles (a dense layer's single expert would give too few work items).
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
 // and the token rows must fit one buffer resource (byte offsets below 2^31).
 static int wide_mode(const Shape& s, int T) {
-  if (s.dense) return kWideNone;
   const long tk = (long)T * s.K;
   if (tk < 32L * s.E) return kWideNone;
   if ((long)T * s.H * 2 >= (1L << 31)) return kWideNone;
   const int wk = s.mx ? 128 : kWWin;   // k per window
   if (s.H % (wk * kWRing) != 0 || s.I % (wk * kWRing) != 0) return kWideNone;
   if (tk <= 64L * s.E)
-    return s.I % WideCfg<kWtBF16, kWGateUp, kWModerateMT, 4>::COLS == 0 &&
+    return !s.dense && s.I % WideCfg<kWtBF16, kWGateUp, kWModerateMT, 4>::COLS == 0 &&
                    s.H % WideCfg<kWtBF16, kWDown, kWModerateMT, 4>::COLS == 0
                ? kWideModerate
                : kWideNone;
@@ -451,10 +455,12 @@ static hipError_t wide_launch(const Shape& s, int T, const uint16_t* act, const 
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* out,
                               hipStream_t stream) {
   using C = WideCfg<WT, MODE, MT, NB>;
-  const long items = (long)max_tiles * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
+  // a dense layer's row tiles all use the same weights: groups of them run each column block together
+  const int tg = s.dense ? kWDenseTileGroup : 1;
+  const long items = (long)((max_tiles + tg - 1) / tg * tg) * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
   const int grid = (int)((items + kWXcds - 1) / kWXcds * kWXcds);
   hipLaunchKernelGGL((wide_kernel<WT, MODE, MT, NB>), dim3(grid), dim3(kWWaves * kWave), 0, stream, s.H, s.I, s.K,
-                     act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2);
+                     act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2, tg);
   return hipGetLastError();
 }
 
