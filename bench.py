@@ -253,7 +253,7 @@ def main():
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
              and w.weight != "mxfp4")
     wk = 128 if w.weight == "mxfp4" else 64      # k per window
-    wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31
+    wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31 and H * I * 2 < 2 ** 31
                and H % (4 * wk) == 0 and I % (4 * wk) == 0)
     wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
                         or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))

@@ -425,11 +425,13 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 //   * MoE layers with 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row
 //     tiles (a dense layer's single expert would give too few work items).
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
-// and the token rows must fit one buffer resource (byte offsets below 2^31).
+// and the token rows and each expert's weight matrix must fit one buffer resource (byte offsets
+// below 2^31).
 static int wide_mode(const Shape& s, int T) {
   const long tk = (long)T * s.K;
   if (tk < 32L * s.E) return kWideNone;
   if ((long)T * s.H * 2 >= (1L << 31)) return kWideNone;
+  if ((long)s.H * s.I * 2 >= (1L << 31)) return kWideNone;   // bf16 bytes bound fp8 and MXFP4 too
   const int wk = s.mx ? 128 : kWWin;   // k per window
   if (s.H % (wk * kWRing) != 0 || s.I % (wk * kWRing) != 0) return kWideNone;
   if (tk <= 64L * s.E)
