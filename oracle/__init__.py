@@ -10,6 +10,11 @@ layer fixes.  See oracle/moe.py for the step-by-step citations.
 
 Parity status of each function:
   codecs.bf16_round_bits / bf16_to_f64 / e4m3_decode  -- pinned (library casts, all codes)
+  codecs.e2m1_decode / mxfp4_unpack / mxfp4_dequant /  -- pinned (torch's own e2m1 conversions:
+  mxfp4_quantize / e8m0_scale                             codes, element rounding, packing; the
+                                                          shared-exponent rule; on-grid round
+                                                          trips; the error bound, saturation and
+                                                          zero blocks; planted mutants caught)
   moe.router_scores / select_experts / route          -- pinned (brute force, invariants,
                                                           the G=1 plain top-k special case)
   moe.permute                                          -- pinned (stable argsort, invariants)
