@@ -103,6 +103,8 @@ ODD_SHAPES = [
     # one-workgroup-per-CU gate/up (375 rows per expert on average: 272-row tiles, tall and short);
     # both one-workgroup-per-CU GEMMs at about 60 rows per expert (96-row tiles), bf16, fp8 and MXFP4
     # (MXFP4 also over two rounds of the four-window ring, whose scale bytes arrive one load per round)
+    # and T*K/E at the schedule boundaries: exactly 32 and 64 rows per expert on average (the 96-row
+    # one-workgroup-per-CU GEMMs), and one token to either side (streaming, LDS-tiled)
     ("h128", 37, 128, 128, 16, 4, 2, 4, 1.0, "bf16"),
     ("g1_k6", 300, 384, 256, 64, 1, 1, 6, 2.5, "bf16"),
     ("all_groups", 700, 256, 256, 32, 8, 8, 8, 2.5, "bf16"),
@@ -112,6 +114,10 @@ ODD_SHAPES = [
     ("moderate_fp8", 240, 512, 256, 32, 8, 4, 8, 2.5, "fp8"),
     ("moderate_mx", 230, 512, 512, 32, 8, 4, 8, 2.5, "mxfp4"),
     ("moderate_mx_2rounds", 220, 1024, 1024, 32, 8, 4, 8, 2.5, "mxfp4"),
+    ("edge_32_rows", 128, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("edge_below_32", 127, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("edge_64_rows", 256, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("edge_above_64", 257, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
 ]
 
 
