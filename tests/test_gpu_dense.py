@@ -38,7 +38,7 @@ def run_dense(w, x_bits, W, deterministic_check=False):
     return C.bits_of(out)
 
 
-@pytest.mark.parametrize("T", [1, 7, 64, 100, 1100, 2000])
+@pytest.mark.parametrize("T", [1, 7, 64, 100, 1024, 1025, 1100, 2000])
 def test_tiny_dense(T):
     w = gen.workload("dense_tiny", T)
     C.say(f"[dense tiny] T={T}")

@@ -104,7 +104,8 @@ ODD_SHAPES = [
     # both one-workgroup-per-CU GEMMs at about 60 rows per expert (96-row tiles), bf16, fp8 and MXFP4
     # (MXFP4 also over two rounds of the four-window ring, whose scale bytes arrive one load per round)
     # and T*K/E at the schedule boundaries: exactly 32 and 64 rows per expert on average (the 96-row
-    # one-workgroup-per-CU GEMMs), and one token to either side (streaming, LDS-tiled)
+    # one-workgroup-per-CU GEMMs) and one token to either side (streaming, LDS-tiled); exactly 192
+    # (the 272-row gate/up) and one token below (LDS-tiled)
     ("h128", 37, 128, 128, 16, 4, 2, 4, 1.0, "bf16"),
     ("g1_k6", 300, 384, 256, 64, 1, 1, 6, 2.5, "bf16"),
     ("all_groups", 700, 256, 256, 32, 8, 8, 8, 2.5, "bf16"),
@@ -118,6 +119,8 @@ ODD_SHAPES = [
     ("edge_below_32", 127, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
     ("edge_64_rows", 256, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
     ("edge_above_64", 257, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("edge_192_rows", 768, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("edge_below_192", 767, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
 ]
 
 
