@@ -76,7 +76,7 @@ typedef struct {
   int32_t hidden;       /* H: multiple of 128 (256 for MXFP4) */
   int32_t inter;        /* I: multiple of 128 (256 for MXFP4) */
   int32_t n_experts;    /* E: 1..256 */
-  int32_t n_groups;     /* G: 1..64, E % G == 0 */
+  int32_t n_groups;     /* G: 1..64, E % G == 0, E/G >= 2 (a group's score sums its two best) */
   int32_t topk_groups;  /* Gk: 1..G */
   int32_t top_k;        /* K: 1..8, K <= Gk * E / G */
   float routed_scale;   /* alpha: finite */

@@ -17,16 +17,11 @@ Readings this module takes where the pages are silent:
   * the norm is RMSNorm with a learned per-channel gain (the only norm the pages
     name, on queries and keys) and an additive epsilon inside the square root:
         n = v / sqrt(mean(v^2) + eps),  out = n * gamma;
-  * "in FP32" is taken literally, one IEEE float32 operation per step: the sum
-    of squares in float32, then one correctly rounded division by H, one
-    addition of eps, one correctly rounded square root and one reciprocal; then
-    v * r, then * gamma;
-  * the pages fix the precision of the sum, not its order.  The order taken:
-    the H channels form 64 contiguous blocks of whole 8-channel chunks (block
-    l holds chunks [l*n/64, (l+1)*n/64), n = H/8, integer division), each
-    block summed in channel order, then the 64 block sums added in block
-    order.  (Any fixed order is an FP32 sum; this one is 64-way parallel, where
-    a single channel-order chain is H dependent additions long.);
+  * "in FP32" is taken literally, one IEEE float32 result per step: the sum
+    of squares is the exact sum rounded once to float32 (the pages fix the
+    precision, not an order of additions, so the definition takes none), then
+    one correctly rounded division by H, one addition of eps, one correctly
+    rounded square root and one reciprocal; then v * r, then * gamma;
   * the stream, the MoE output and both norm outputs are bf16 (the model dtype),
     each norm output rounded once to nearest-even;
   * the mix is new = bf16( f32(a * stream) + f32(b * post) ) with the weights
@@ -46,34 +41,45 @@ from .codecs import bf16_round_bits, bf16_to_f64
 from .moe import LayerSpec, forward
 
 
-NORM_BLOCKS = 64
+def _round_f32_exact(sq: np.ndarray) -> np.float32:
+    """The exact sum of the float64 values sq (each exact), rounded once to float32 (nearest, ties to even).
 
-
-def norm_block_bounds(H: int):
-    """Channel ranges [lo, hi) of the 64 summation blocks of an H-channel row (H % 8 == 0)."""
-    if H % 8:
-        raise ValueError("the norm takes rows of a multiple of 8 channels")
-    n = H // 8
-    return [(8 * (l * n // NORM_BLOCKS), 8 * ((l + 1) * n // NORM_BLOCKS)) for l in range(NORM_BLOCKS)]
+    math.fsum returns the exact sum rounded to float64.  Rounding that to
+    float32 can round twice only when it lands exactly halfway between two
+    float32 values; then the sign of the exact remainder (fsum of the terms
+    minus that midpoint, whose sign fsum gets right) decides the direction.
+    """
+    s64 = math.fsum(sq)
+    r = np.float32(s64)
+    if not np.isfinite(r) or float(r) == s64:
+        return r
+    other = np.nextafter(r, np.float32(np.inf) if float(r) < s64 else np.float32(-np.inf))
+    if s64 - float(r) != float(other) - s64:            # not a float32 midpoint: one rounding
+        return r
+    rem = math.fsum(list(sq) + [-s64])                   # exact sum minus the midpoint, sign exact
+    if rem == 0.0:
+        return r                                         # a true tie: numpy already chose the even one
+    up = rem > 0.0
+    lo, hi = (r, other) if float(r) < float(other) else (other, r)
+    return hi if up else lo
 
 
 def sum_squares_f32(v) -> np.ndarray:
-    """float32 sum of squares of float32 rows [T, H] in the block order above."""
+    """float32 sum of squares of float32 rows [T, H]: the exact sum, rounded once.
+
+    The rows are bf16 values, so each square is exact in float64 (16 significant
+    bits), and the float32 result does not depend on an order of additions.
+    """
     v = np.asarray(v, np.float32)
-    T, H = v.shape
-    total = np.zeros(T, np.float32)
-    for lo, hi in norm_block_bounds(H):
-        part = np.zeros(T, np.float32)
-        for h in range(lo, hi):                  # one block, channel order
-            part = part + v[:, h] * v[:, h]      # float32 * float32 and + float32: one rounding each
-        total = total + part                     # block sums in block order
-    return total
+    sq = v.astype(np.float64) ** 2
+    return np.array([_round_f32_exact(row) for row in sq], np.float32)
 
 
 def rms_norm_bits(v_bits, gamma, eps: float) -> np.ndarray:
     """RMSNorm of bf16 rows [T, H] with float32 gain gamma [H] -> bf16 bits [T, H].
 
-    Sum of squares in float32 (sum_squares_f32); then ms = ss / H,
+    Sum of squares: the exact sum rounded once to float32 (sum_squares_f32);
+    then ms = ss / H,
     r = 1 / sqrt(ms + eps), out = bf16((v * r) * gamma), each step one float32
     operation.
     """

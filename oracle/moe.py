@@ -93,7 +93,9 @@ def router_scores(x_bits, w_router, b_router) -> np.ndarray:
 
 
 def _group_scores(s: np.ndarray, spec: LayerSpec) -> np.ndarray:
-    """Group score = f32(top1 + top2) of the group's sigmoid scores."""
+    """Group score = f32(top1 + top2) of the group's sigmoid scores (a group holds at least two experts)."""
+    if spec.group_size < 2:
+        raise ValueError("a group's score is the sum of its two best scores: groups need two experts or more")
     T = s.shape[0]
     sg = np.sort(s.reshape(T, spec.n_groups, spec.group_size).astype(np.float64), axis=2)
     return f32(sg[:, :, -1] + sg[:, :, -2])

@@ -25,6 +25,8 @@ int check_config(const beam_moe_config* c) {
       c->top_k <= 0)
     return BEAM_MOE_ERR_INVALID;
   if (c->n_experts % c->n_groups != 0) return BEAM_MOE_ERR_INVALID;
+  // a group's score is the sum of its two best scores: every group holds at least two experts
+  if (c->n_experts / c->n_groups < 2) return BEAM_MOE_ERR_INVALID;
   if (c->topk_groups > c->n_groups) return BEAM_MOE_ERR_INVALID;
   if ((long)c->top_k > (long)c->topk_groups * (c->n_experts / c->n_groups)) return BEAM_MOE_ERR_INVALID;
   if (!isfinite(c->routed_scale)) return BEAM_MOE_ERR_INVALID;

@@ -56,6 +56,9 @@ BAD_CONFIGS = [
     (dict(n_experts=512, n_groups=8), B.ERR_UNSUPPORTED),
     (dict(top_k=9, topk_groups=4), B.ERR_UNSUPPORTED),
     (dict(n_groups=128, n_experts=256, topk_groups=8), B.ERR_UNSUPPORTED),
+    # one expert per group: a group score is the sum of a group's two best scores
+    (dict(n_experts=32, n_groups=32, topk_groups=8), B.ERR_INVALID),
+    (dict(n_experts=8, n_groups=8, topk_groups=8, top_k=8), B.ERR_INVALID),
 ]
 
 

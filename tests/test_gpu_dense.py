@@ -71,15 +71,13 @@ def test_real_shape_dense(name, n_sample):
 
 
 def test_spec_verify_shape():
-    from tests.test_gpu_parity import real_weights
+    from tests.test_gpu_parity import real_source, real_weights
     w = gen.workload("spec_verify")
     C.say(f"[spec_verify] T={w.T}")
     spec, x, wr, b = C.guarded(w, 0)
     out, ids, wts = C.run_forward(w, *C.router_tensors(x, wr, b), real_weights("bf16"))
     rid, rw = oracle.route(spec, x, wr, b)
     C.check_ids_w(ids.cpu().numpy(), wts.cpu().numpy(), rid, rw)
-    sample = np.array([0, 17, 64, w.T - 1])
-    src = gen.ExpertSource(w, 0)
-    src.prefetch(np.unique(rid[sample]))
-    ref = oracle.forward(spec, x[sample], wr, b, src.get)
-    C.check_out(C.bits_of(out)[sample], ref["out"])
+    sample = np.arange(w.T)        # every token of the verify batch
+    ref = C.oracle_forward_threads(spec, x[sample], wr, b, real_source("bf16").get)
+    C.check_out(C.bits_of(out)[sample], ref["out"], what="spec_verify output")

@@ -1,6 +1,8 @@
 """Pins for the oracle's norms and residual mix (oracle/block.py), against what
 the pages and the mathematics fix, not against the oracle's own formula:
 
+  * the sum of squares: the exact sum rounded once (cases where a float32 chain or a
+    second rounding of the float64 sum give other values), independent of channel order;
   * RMSNorm against an exactly summed (math.fsum) float64 reference, within one
     bf16 ulp, at magnitudes where eps matters and at a width where H vs H-1 shows;
   * closed forms for constant rows; exact invariance under power-of-two scaling;
@@ -47,25 +49,57 @@ def test_rms_norm_within_one_ulp_of_exact(sigma, eps, H):
     assert np.all(got[~nz] == 0)
 
 
-def test_sum_squares_block_order():
-    """The stated order, by hand: a big square first, then unit squares.  Channel order would
-    absorb every +1 into 2^24 (ties to even); the block order first sums each block's units
-    exactly and adds the block sums, which survive.  H = 5120: blocks of 80 channels, so the
-    big value in channel 79 (the last of block 0) leaves blocks 1..63 with 80 units each; a
-    block boundary one channel off gives a different total."""
+def _squares_row(vals, H=128):
+    v = np.zeros((1, H), np.float32)
+    v[0, :len(vals)] = vals
+    assert np.array_equal(codecs.bf16_to_f64(_bf16(v)), v.astype(np.float64))   # bf16 values
+    return v
+
+
+def test_sum_squares_is_the_exact_sum_rounded_once():
+    """The definition fixes no order of additions: the float32 sum of squares is the exact sum,
+    rounded once.  Cases built so that the plausible shortcuts give other answers:
+      * a square of 2^24 then 5040 unit squares: exact 2^24 + 5040 (a float32 value); a float32
+        chain in channel order absorbs every +1 (ties to even) and gives 2^24;
+      * exact 1 + 2^-24 + 2^-80, just above the float32 midpoint between 1 and 1 + 2^-23:
+        rounds up; the float64 sum lands on the midpoint and a second rounding (ties to even)
+        gives 1;
+      * exact 1 + 3*2^-24 - 2^-80 (the 2^-80 deficit from three copies of each 4^-j,
+        j = 13..40), just below the midpoint between 1 + 2^-23 and 1 + 2^-22: rounds down; a
+        second rounding of the float64 sum gives 1 + 2^-22."""
     v = np.zeros((1, 5120), np.float32)
-    v[0, 79] = 4096.0                      # square 2^24
+    v[0, 79] = 4096.0
     v[0, 80:] = 1.0
-    assert block.norm_block_bounds(5120)[:2] == [(0, 80), (80, 160)]
-    assert block.sum_squares_f32(v)[0] == np.float32(2.0 ** 24 + 63 * 80)
+    assert block.sum_squares_f32(v)[0] == np.float32(2.0 ** 24 + 5040)
     seq = np.float32(0)
     for h in range(5120):
         seq = np.float32(seq + v[0, h] * v[0, h])
-    assert seq == np.float32(2.0 ** 24)    # what channel order would give
-    # fewer than 64 chunks: empty blocks add nothing; every chunk is summed exactly once
-    w = np.arange(1, 25, dtype=np.float32)[None, :] / 8
-    assert block.sum_squares_f32(w)[0] == np.float32(np.sum(np.float64(w) ** 2))
-    assert sum(hi - lo for lo, hi in block.norm_block_bounds(24)) == 24
+    assert seq == np.float32(2.0 ** 24)               # what a channel-order float32 chain gives
+
+    up = _squares_row([1.0, 2.0 ** -12, 2.0 ** -40])
+    assert block.sum_squares_f32(up)[0] == np.float32(1 + 2.0 ** -23)
+    assert np.float32(math.fsum(np.float64(up[0]) ** 2)) == np.float32(1.0)      # double rounding
+
+    down_vals = [1.0, 2.0 ** -12, 2.0 ** -12] + [2.0 ** -j for j in range(13, 41) for _ in range(3)]
+    down = _squares_row(down_vals)
+    assert block.sum_squares_f32(down)[0] == np.float32(1 + 2.0 ** -23)
+    assert np.float32(math.fsum(np.float64(down[0]) ** 2)) == np.float32(1 + 2.0 ** -22)
+
+    # an exact tie stays a tie: 1 + 2^-24 goes to the even neighbour, 1
+    assert block.sum_squares_f32(_squares_row([1.0, 2.0 ** -12]))[0] == np.float32(1.0)
+
+
+def test_sum_squares_does_not_depend_on_channel_order():
+    rng = np.random.default_rng(17)
+    v = codecs.bf16_to_f64(_bf16(rng.standard_normal((6, 5120)) * np.exp2(rng.integers(-20, 20, (6, 5120)))))
+    v = v.astype(np.float32)
+    ref = block.sum_squares_f32(v)
+    for seed in range(3):
+        perm = np.random.default_rng(seed).permutation(5120)
+        assert np.array_equal(block.sum_squares_f32(v[:, perm]), ref)
+    g = np.ones(5120, np.float32)
+    perm = np.random.default_rng(5).permutation(5120)
+    assert np.array_equal(oracle.rms_norm_bits(_bf16(v)[:, perm], g, 1e-6), oracle.rms_norm_bits(_bf16(v), g, 1e-6)[:, perm])
 
 
 def test_rms_norm_constant_rows_closed_form():
@@ -174,11 +208,26 @@ def _swapped_mix_weights(step):
     return b, a
 
 
+def _sum_squares_channel_chain(v):
+    v = np.asarray(v, np.float32)
+    acc = np.zeros(v.shape[0], np.float32)
+    for h in range(v.shape[1]):
+        acc = acc + v[:, h] * v[:, h]
+    return acc
+
+
+def _sum_squares_rounded_twice(v):
+    v = np.asarray(v, np.float32)
+    return np.array([np.float32(math.fsum(np.float64(r) ** 2)) for r in v], np.float32)
+
+
 BLOCK_MUTANTS = [
     ("rms_norm_bits", _eps_outside_sqrt, [lambda: test_rms_norm_within_one_ulp_of_exact(1e-3, 1e-6, 64)]),
     ("rms_norm_bits", _mean_over_h_minus_1, [lambda: test_rms_norm_within_one_ulp_of_exact(1.0, 1e-6, 64)]),
     ("rms_norm_bits", _no_gain, [test_rms_norm_constant_rows_closed_form]),
     ("mix_weights", _swapped_mix_weights, [test_mix_keeps_unit_scale_and_weights_the_new_output_less_with_depth]),
+    ("sum_squares_f32", _sum_squares_channel_chain, [test_sum_squares_is_the_exact_sum_rounded_once]),
+    ("sum_squares_f32", _sum_squares_rounded_twice, [test_sum_squares_is_the_exact_sum_rounded_once]),
 ]
 
 
@@ -186,7 +235,8 @@ BLOCK_MUTANTS = [
 def test_block_mutant_is_caught(monkeypatch, name, mutant, pins):
     monkeypatch.setitem(block.__dict__, "_orig_" + name, getattr(block, name))
     monkeypatch.setattr(block, name, mutant)
-    monkeypatch.setattr(oracle, name, mutant)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, mutant)
     for pin in pins:
         with pytest.raises(AssertionError):
             pin()

@@ -54,6 +54,25 @@ def _dropped_bias(x_bits, w_router, b_router):
     return moe.__dict__["_orig_router_logits"](x_bits, w_router, None)
 
 
+def _gap_variant(dg=0, dk=0, all_groups=False):
+    """gap_violations with the group boundary at Gk + dg, the expert boundary at K + dk, or the
+    expert candidates taken from every group."""
+    def f(spec, x_bits, w_router, b_router, guard=moe.GAP_GUARD):
+        s = moe.router_scores(x_bits, w_router, b_router)
+        gs = np.sort(moe._group_scores(s, spec).astype(np.float64), axis=1)[:, ::-1]
+        gk, k = spec.topk_groups + dg, spec.top_k + dk
+        bad = (gs[:, gk - 1] - gs[:, gk]) < guard
+        _, kept = moe.select_experts(s, spec)
+        in_kept = np.zeros((s.shape[0], spec.n_groups), bool)
+        np.put_along_axis(in_kept, kept, True, axis=1)
+        cand = np.ones_like(s, bool) if all_groups else np.repeat(in_kept, spec.group_size, axis=1)
+        key = np.sort(np.where(cand, s.astype(np.float64), -np.inf), axis=1)[:, ::-1]
+        bad |= (key[:, k - 1] - key[:, k]) < guard
+        return np.nonzero(bad)[0]
+    f.__name__ = f"gap_dg{dg}_dk{dk}" + ("_all_groups" if all_groups else "")
+    return f
+
+
 MUTANTS = [
     ("_group_scores", _top1_group_scores, [lambda: R.test_selection_brute_force(0)]),
     ("combine_weights", _unnormalised_weights, [R.test_weights_exact_normalisation]),
@@ -63,6 +82,11 @@ MUTANTS = [
     ("permute", _unstable_permute, [lambda: P.test_permute_vs_counting_sort("tiny", None)]),
     ("expert_rows", _swapped_swiglu, [X.test_expert_naive_loops]),
     ("combine", _combine_wrong_index, [X.test_combine_fixed_order, lambda: X.test_identical_experts_equal_dense_mlp(0)]),
+    ("gap_violations", _gap_variant(dg=-1), [R.test_gap_violations_boundary_positions]),
+    ("gap_violations", _gap_variant(dg=+1), [R.test_gap_violations_boundary_positions]),
+    ("gap_violations", _gap_variant(dk=-1), [R.test_gap_violations_boundary_positions]),
+    ("gap_violations", _gap_variant(dk=+1), [R.test_gap_violations_boundary_positions]),
+    ("gap_violations", _gap_variant(all_groups=True), [R.test_gap_violations_boundary_positions]),
 ]
 
 

@@ -169,3 +169,76 @@ def test_gap_guard_redraws():
     assert len(oracle.gap_violations(spec, x, wr, b, guard=1.0)) == w.T
     x2, wr2, b2, n = gen.guarded_router_inputs(w, 0, lambda x, wr, b: oracle.gap_violations(spec, x, wr, b))
     assert len(oracle.gap_violations(spec, x2, wr2, b2)) == 0
+
+
+def _hand_routing(logit_rows):
+    """x row t = the unit vector e_t (bf16 1.0) and W_router row t = token t's logits, so each
+    token's fp32 logits are exactly the given values (rounded once to fp32)."""
+    T, E = len(logit_rows), len(logit_rows[0])
+    H = 256
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), np.arange(T)] = 0x3F80            # bf16 1.0
+    wr = np.zeros((H, E), np.float32)
+    wr[:T] = np.asarray(logit_rows, np.float32)
+    return x, wr
+
+
+def test_gap_violations_boundary_positions():
+    """Hand-built tiny routings (8 groups of 4, Gk = 4, K = 8), one boundary gap of about 4e-7 per
+    token and every other gap wide.  Only a close pair AT a selection boundary (the 4th vs 5th group
+    score; the 8th vs 9th candidate inside the kept groups) flags a token: the same close pair one
+    position earlier or later, or among the experts of a dropped group, does not.  Each boundary
+    index off by one, or candidates taken from every group, changes the flagged set."""
+    spec = oracle.LayerSpec(256, 128, 32, 8, 4, 8, 2.5)
+    eps = 2.5e-6                         # logit step near 1.4-2: a score step of about 4e-7
+    low = -3.0
+    rank_to_group = [5, 2, 7, 0, 3, 6, 1, 4]            # group of the r-th best group
+    slot = [2, 0, 3, 1]                                 # expert position in the group of its r-th value
+
+    def row(groups):
+        """groups[r] = the 4 logits of the r-th ranked group, best first."""
+        z = np.full(32, low, np.float64)
+        for r, vals in enumerate(groups):
+            g = rank_to_group[r]
+            for j, v in enumerate(vals):
+                z[4 * g + slot[j]] = v
+        return z
+
+    base = [[3.0, 2.9, low, low], [2.5, 2.4, low, low], [2.0, 1.9, low, low], [1.5, 1.4, low, low],
+            [1.0, 0.9, low, low], [0.5, 0.4, low, low], [0.0, -0.1, low, low], [-0.5, -0.6, low, low]]
+
+    def variant(changes):
+        g = [list(v) for v in base]
+        for (r, j), v in changes.items():
+            g[r][j] = v
+        return row(g)
+
+    rows = [
+        variant({(4, 0): 1.5, (4, 1): 1.4 - eps}),           # 0: 4th vs 5th group score: flagged
+        variant({(3, 0): 2.0, (3, 1): 1.9 - eps}),           # 1: 3rd vs 4th group (and 7th vs 8th expert)
+        variant({(5, 0): 1.0, (5, 1): 0.9 - eps}),           # 2: 5th vs 6th group
+        variant({(0, 2): 1.4 - eps}),                        # 3: 8th vs 9th candidate: flagged
+        variant({(3, 1): 1.5 - eps}),                        # 4: 7th vs 8th candidate
+        variant({(0, 2): 0.5, (0, 3): 0.5 - eps}),           # 5: 9th vs 10th candidate
+        variant({}),                                         # 6: every gap wide
+        variant({(4, 0): 1.4 - eps}),                        # 7: a dropped group's expert next to the 8th
+    ]
+    x, wr = _hand_routing(rows)
+    b = np.zeros(32, np.float32)
+    # the fixture does what it says: the designed gaps are in (0, 1e-6), the rest far wider
+    s = oracle.router_scores(x, wr, b).astype(np.float64)
+    gs = np.sort(oracle.moe._group_scores(s.astype(np.float32), spec).astype(np.float64), axis=1)[:, ::-1]
+    assert 0 < gs[0, 3] - gs[0, 4] < 1e-6 and 0 < gs[1, 2] - gs[1, 3] < 1e-6 and 0 < gs[2, 4] - gs[2, 5] < 1e-6
+    assert np.all(np.diff(-gs[6]) > 1e-3)
+    ids, kept = oracle.select_experts(s.astype(np.float32), spec)
+    assert [sorted(int(rank_to_group.index(g)) for g in kept[t]) for t in (3, 4, 5, 6, 7)] == [[0, 1, 2, 3]] * 5
+    assert list(oracle.gap_violations(spec, x, wr, b)) == [0, 3]
+    # a guard below the designed gaps flags nothing
+    assert list(oracle.gap_violations(spec, x, wr, b, guard=1e-9)) == []
+
+
+def test_group_size_one_is_rejected():
+    spec = oracle.LayerSpec(256, 128, 8, 8, 4, 4, 2.5)
+    s = np.full((2, 8), 0.5, np.float32)
+    with pytest.raises(ValueError):
+        oracle.select_experts(s, spec)
