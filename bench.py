@@ -17,6 +17,14 @@ TFLOP/s with their fractions of MI355X's peaks, a roofline entry for the
 dominant kernel (gate/up), every stage kernel against its own roofline
 (stages), and the CPU oracle timed on a bounded sample of the same workload
 on this machine's host cores.
+
+The metric has two halves: HBM GB/s at decode and MFMA TFLOP/s at prefill.
+The default run (the decode workload, T = 64) therefore also measures the
+balanced prefill workload (T = 8192) on the same expert weights and puts it
+in the same line as "prefill" (ms, tokens/s, MFMA TFLOP/s and fraction,
+stage rooflines, its own CPU-oracle sample); --no-prefill leaves it out.
+--steps / --warmup set the headline workload's counts; the prefill part
+uses its own defaults.
 """
 from __future__ import annotations
 
@@ -72,6 +80,16 @@ def load_traffic(workload, kernel, kind):
     return d.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
     """The oracle as it stands, on a bounded token sample of the same workload (host cores)."""
     import oracle
@@ -92,7 +110,8 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
             total_tok += min(n, w.T - start)
             if total_t > seconds_target * 0.5:
                 break
-        return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "cpu": cpu_model(),
+                "kind": "oracle",
                 "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), dense MLP per token, "
                           f"{total_t:.1f} s of oracle time, weight generation excluded"}
     spec = oracle.LayerSpec.of(w)
@@ -116,78 +135,55 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
         start = sel.stop
         if total_t > seconds_target * 0.5:
             break
-    return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": total_tok / total_t, "unit": "tokens/s", "cores": int(threads), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{total_tok} tokens of the {w.name} batch (T={w.T}), "
                       f"{'whole sublayer' if block else 'full layer'} per token, "
                       f"{total_t:.1f} s of oracle time, weight generation excluded"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--block", action="store_true",
-                    help="time the whole sublayer: pre-norm, the MoE block, post-norm and the residual mix "
-                         "(beam_moe_block_forward, step 23 = layer 10's MoE sublayer)")
-    ap.add_argument("--no-stage-events", action="store_true",
-                    help="time the steps without the per-stage events (no roofline entry)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
-                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
-              "sharding is not built here", file=sys.stderr)
-        sys.exit(2)
-    steps, warmup = DEFAULTS[args.workload]
-    steps = args.steps if args.steps is not None else steps
-    warmup = args.warmup if args.warmup is not None else warmup
+def gateup_kind(w):
+    """Which gate/up kernel family the library runs for this workload (mirrors its schedule choice):
+    LDS-tiled from 32 rows per expert (the dense path streams up to 1024 tokens); the
+    one-workgroup-per-CU kernel for MoE layers at 32..64 rows per expert (any weight type), and from
+    192 rows per expert (bf16) wherever the LDS-tiled one would run, dense included."""
+    dense = w.n_experts == 1
+    TK, H, I = w.T * w.top_k, w.hidden, w.inter
+    tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
+             and w.weight != "mxfp4")
+    wk = 128 if w.weight == "mxfp4" else 64      # k per window
+    wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31 and H * I * 2 < 2 ** 31
+               and H % (4 * wk) == 0 and I % (4 * wk) == 0)
+    wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
+                        or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))
+    return "wide" if wide else ("tiled" if tiled else "stream")
 
+
+def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, seed=0):
+    """Time `steps` forward passes of workload w on resident inputs; returns the workload's figures."""
     import torch
     import sparse_moe_layer_top_amd as bm
     from synth import gen
 
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        a = torch.ones(n, dtype=torch.uint8, device=dev)
-        c = torch.empty_like(a)
-        for _ in range(5):
-            c.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
-        return
-    w = gen.workload(args.workload)
     wtype = {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight]
     cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha, wtype)
-    log(f"[bench] {w.name}: T={w.T} H={w.hidden} I={w.inter} E={w.n_experts} weights={w.weight}")
-    x_bits, wr, b = gen.router_inputs(w, args.seed)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     wr_t = torch.from_numpy(wr).to(dev)
     b_t = torch.from_numpy(b).to(dev)
-    t0 = time.time()
-    W = gen.device_expert_weights(w, args.seed, dev, log=log)
-    log(f"[bench] expert weights on device in {time.time() - t0:.1f} s")
     out = torch.empty(w.T, w.hidden, dtype=torch.bfloat16, device=dev)
     ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device=dev)
     wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=dev)
     ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
 
     dense = w.n_experts == 1
-    if dense and args.block:
-        print("--block applies to the MoE workloads", file=sys.stderr)
-        sys.exit(2)
-    stages = BLOCK_STAGES if args.block else (DENSE_STAGES if dense else STAGES)
+    stages = BLOCK_STAGES if block else (DENSE_STAGES if dense else STAGES)
     if dense:
         dcfg = bm.DenseConfig(w.hidden, w.inter, wtype)
         Wd = {k: v[0] for k, v in W.items()}
         ws = torch.empty(max(1, bm.beam_dense_workspace_bytes(dcfg, w.T)), dtype=torch.uint8, device=dev)
-    if args.block:
-        gpre, gpost = (torch.from_numpy(g).to(dev) for g in gen.norm_gains(w, args.seed))
+    if block:
+        gpre, gpost = (torch.from_numpy(g).to(dev) for g in gen.norm_gains(w, seed))
         stream_out = torch.empty_like(x)
         ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T, bm.OP_BLOCK), dtype=torch.uint8, device=dev)
 
@@ -195,7 +191,7 @@ def main():
         if dense:
             bm.beam_dense_mlp_forward(dcfg, x, Wd["gate"], Wd["up"], Wd["down"], Wd.get("s_gate"), Wd.get("s_up"),
                                       Wd.get("s_down"), out=out, workspace=ws, stage_events=events)
-        elif args.block:
+        elif block:
             bm.beam_moe_block_forward(cfg, BLOCK_STEP, BLOCK_EPS, x, gpre, gpost, wr_t, b_t, W["gate"], W["up"],
                                       W["down"], W.get("s_gate"), W.get("s_up"), W.get("s_down"),
                                       stream_out=stream_out, topk_ids_out=ids, topk_w_out=wts, workspace=ws,
@@ -215,15 +211,15 @@ def main():
             e.record()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    log(f"[bench] timing {steps} steps")
+    log(f"[bench] {w.name}: timing {steps} steps")
     start.record()
     for i in range(steps):
-        step(None if args.no_stage_events else evs[i])
+        step(evs[i] if stage_events else None)
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
-    stage_ms = {name: (float("nan") if args.no_stage_events else
-                       float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])))
+    stage_ms = {name: (float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                       if stage_events else float("nan"))
                 for j, name in enumerate(stages)}
 
     # routing statistics and algorithmic work of this batch
@@ -244,20 +240,19 @@ def main():
         layer_bytes += H * w.n_experts * 4 + w.n_experts * 4          # router weights and bias
     layer_flops = 6.0 * TK * H * I
     gu_flops = 4.0 * TK * H * I
-    s = ms / 1e3
-    hbm_gbps = layer_bytes / s / 1e9
-    tflops = layer_flops / s / 1e12
-    # the library's gate/up kernel: LDS-tiled from 32 rows per expert (the dense path streams up to 1024
-    # tokens); the one-workgroup-per-CU kernel for MoE layers at 32..64 rows per expert (any weight
-    # type), and from 192 rows per expert (bf16) wherever the LDS-tiled one would run, dense included
-    tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
-             and w.weight != "mxfp4")
-    wk = 128 if w.weight == "mxfp4" else 64      # k per window
-    wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31 and H * I * 2 < 2 ** 31
-               and H % (4 * wk) == 0 and I % (4 * wk) == 0)
-    wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
-                        or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))
-    kind = "wide" if wide else ("tiled" if tiled else "stream")
+    sec = ms / 1e3
+    hbm_gbps = layer_bytes / sec / 1e9
+    tflops = layer_flops / sec / 1e12
+    kind = gateup_kind(w)
+    res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / sec, 1),
+           "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
+           "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "layer_bytes": layer_bytes, "layer_flops": layer_flops,
+           "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+           "routing": None if dense else {"touched_experts": D, "max_load": int(load.max()),
+                                          "mean_load": TK / w.n_experts, "zero_load_experts": int((load == 0).sum())}}
+    if not stage_events:
+        return res
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
     gbps = gu_bytes / t_gu / 1e9
@@ -307,29 +302,9 @@ def main():
         ent["bound"] = "mfma" if mfma_floor > hbm_floor else "hbm"
         ent["frac"] = round(max(hbm_floor, mfma_floor) / t, 4)
         stages_roof[name] = ent
-
-    res = {
-        "metric": METRIC, "value": round(w.T / s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 MFMA",
-                                       "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 MFMA"}[w.weight],
-        "data": "synthetic (seeded, random-init weights of the real layer shape)",
-        "config": {"workload": (f"{w.name}: T={w.T}, dense SwiGLU MLP, hidden {H}, inter {I}" if dense else
-                                f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
-                                f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}")
-                               + (f"; whole sublayer: RMSNorm before and after, residual mix at step {BLOCK_STEP}"
-                                  if args.block else ""),
-                   "T": w.T, "weights": w.weight, "bias": w.bias},
-        "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
-        "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "layer_bytes": layer_bytes, "layer_flops": layer_flops,
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "routing": None if dense else {"touched_experts": D, "max_load": int(load.max()),
-                                       "mean_load": TK / w.n_experts, "zero_load_experts": int((load == 0).sum())},
-        "roofline": roof,
-        "stages": stages_roof,
-    }
-    if args.block:
+    res["roofline"] = roof
+    res["stages"] = stages_roof
+    if block:
         # the two norm kernels: rows read and written (plus the combine's y reads for the fused one)
         norm_bytes = 2 * w.T * H * 2 + H * 4
         cnm_bytes = TK * H * 2 + 2 * w.T * H * 2 + H * 4 + TK * 8
@@ -337,9 +312,97 @@ def main():
                         "pre_norm_GBps": round(norm_bytes / (stage_ms["pre_norm"] / 1e3) / 1e9, 1),
                         "combine_norm_mix_GBps": round(cnm_bytes / (stage_ms["combine_norm_mix"] / 1e3) / 1e9, 1),
                         "pre_norm_bytes": norm_bytes, "combine_norm_mix_bytes": cnm_bytes}
+    return res
+
+
+def describe(w, block=False):
+    H, I = w.hidden, w.inter
+    return ((f"{w.name}: T={w.T}, dense SwiGLU MLP, hidden {H}, inter {I}" if w.n_experts == 1 else
+             f"{w.name}: T={w.T}, hidden {H}, {w.n_experts} SwiGLU experts of inter {I}, "
+             f"{w.n_groups} groups, top-{w.topk_groups} groups, top-{w.top_k}, x{w.alpha}")
+            + (f"; whole sublayer: RMSNorm before and after, residual mix at step {BLOCK_STEP}" if block else ""))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(DEFAULTS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the decode workload, leave out the balanced prefill part of the line")
+    ap.add_argument("--block", action="store_true",
+                    help="time the whole sublayer: pre-norm, the MoE block, post-norm and the residual mix "
+                         "(beam_moe_block_forward, step 23 = layer 10's MoE sublayer)")
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="time the steps without the per-stage events (no roofline entry)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is not built here", file=sys.stderr)
+        sys.exit(2)
+    steps, warmup = DEFAULTS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+
+    import torch
+    import sparse_moe_layer_top_amd  # noqa: F401  (fails loudly if the library is not built)
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        c = torch.empty_like(a)
+        for _ in range(5):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+    w = gen.workload(args.workload)
+    if w.n_experts == 1 and args.block:
+        print("--block applies to the MoE workloads", file=sys.stderr)
+        sys.exit(2)
+    log(f"[bench] {w.name}: T={w.T} H={w.hidden} I={w.inter} E={w.n_experts} weights={w.weight}")
+    x_bits, wr, b = gen.router_inputs(w, args.seed)
+    t0 = time.time()
+    W = gen.device_expert_weights(w, args.seed, dev, log=log)
+    log(f"[bench] expert weights on device in {time.time() - t0:.1f} s")
+    m = measure(w, W, x_bits, wr, b, steps, warmup, block=args.block, stage_events=not args.no_stage_events,
+                seed=args.seed)
+
+    res = {
+        "metric": METRIC, "value": m["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 MFMA",
+                                       "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 MFMA"}[w.weight],
+        "data": "synthetic (seeded, random-init weights of the real layer shape)",
+        "config": {"workload": describe(w, args.block), "T": w.T, "weights": w.weight, "bias": w.bias},
+    }
+    res.update({k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")})
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, x_bits, wr, b, block=args.block)
+
+    # the prefill half of the metric: balanced prefill on the same expert weights (MFMA TFLOP/s vs peak)
+    if args.workload == "decode" and not args.block and not args.no_prefill:
+        wp = gen.workload("prefill")
+        assert wp.weights_id == w.weights_id and wp.weight == w.weight
+        psteps, pwarm = DEFAULTS["prefill"]
+        px, pwr, pb = gen.router_inputs(wp, args.seed)
+        pm = measure(wp, W, px, pwr, pb, psteps, pwarm, stage_events=not args.no_stage_events, seed=args.seed)
+        pref = {"workload": describe(wp), "T": wp.T, "bias": wp.bias, "steps": psteps, "warmup": pwarm,
+                "target": {"ms_per_step": 4.10, "mfma_frac": 0.5}}
+        pref.update(pm)
+        if not args.no_cpu_baseline:
+            log("[bench] CPU oracle baseline (prefill)")
+            pref["cpu_baseline"] = cpu_baseline(wp, px, pwr, pb)
+        res["prefill"] = pref
     print(json.dumps(res), flush=True)
 
 

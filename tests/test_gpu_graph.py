@@ -1,0 +1,85 @@
+"""beam_moe_forward captured into a HIP graph (torch.cuda.graph on a side stream) and replayed:
+the forward enqueues kernels only (no host sync, no allocation, no memset), so a captured call
+must give the same bytes as a direct call on every replay, read its input buffers as they are at
+replay time, and meet the oracle's bar.  Replays are separated by the program's own eager work
+(a direct call on other inputs, a fill of the output) and synchronisations."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import gen
+from tests import gpu_cases as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture_and_replay(w, W, seeds, src=None):
+    import sparse_moe_layer_top_amd as bm
+    cfg = C.cfg_of(w)
+    d = C.dev()
+    inputs = [C.guarded(w, s) for s in seeds]
+    xt = C.to_bf16(inputs[0][1])
+    wrt = torch.from_numpy(inputs[0][2]).to(d)
+    bt = torch.from_numpy(inputs[0][3]).to(d)
+    out = torch.empty(w.T, w.hidden, dtype=torch.bfloat16, device=d)
+    ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device=d)
+    wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=d)
+    ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=d)
+
+    def call():
+        bm.beam_moe_forward(cfg, xt, wrt, bt, W["gate"], W["up"], W["down"], W.get("s_gate"), W.get("s_up"),
+                            W.get("s_down"), out=out, topk_ids_out=ids, topk_w_out=wts, workspace=ws)
+
+    # direct results for every input set, with separate buffers
+    direct = []
+    for spec, x, wr, b in inputs:
+        o, i, ww = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+        direct.append((C.bits_of(o), i.cpu().numpy(), ww.cpu().numpy()))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        k = rep % len(inputs)
+        _, x, wr, b = inputs[k]
+        xt.copy_(C.to_bf16(x))                   # new inputs into the captured buffers (eager)
+        wrt.copy_(torch.from_numpy(wr))
+        bt.copy_(torch.from_numpy(b))
+        out.fill_(float("nan"))
+        ids.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        C.say(f"[graph {w.name}] replay {rep}: input set {k}")
+        o, i, ww = direct[k]
+        assert np.array_equal(C.bits_of(out), o), f"replay {rep}: output bytes differ from the direct call"
+        assert np.array_equal(ids.cpu().numpy(), i)
+        assert np.array_equal(wts.cpu().numpy().view(np.uint32), ww.view(np.uint32))
+        # eager work between replays: a direct call on the other input set
+        C.run_forward(w, *C.router_tensors(*inputs[(k + 1) % len(inputs)][1:]), W)
+    return inputs, direct
+
+
+def test_graph_tiny():
+    w = gen.workload("tiny", 300)
+    W, src = C.host_expert_weights(w, 2)
+    inputs, direct = _capture_and_replay(w, W, seeds=[2, 3])
+    for (spec, x, wr, b), (o, i, ww) in zip(inputs, direct):
+        ref = oracle.forward(spec, x, wr, b, src.get)
+        C.check_ids_w(i, ww, ref["ids"], ref["w"])
+        C.check_out(o, ref["out"], what="graph tiny output")
+
+
+def test_graph_decode():
+    from tests.test_gpu_parity import real_weights
+    w = gen.workload("decode")
+    _capture_and_replay(w, real_weights("bf16"), seeds=[0, 1])
