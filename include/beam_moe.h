@@ -163,6 +163,30 @@ int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T,
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
 
+/* Allocation-free forward, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation and kernels as beam_moe_forward (bit-identical results), with
+ * its workspace in a fixed device array inside this library instead of a caller
+ * buffer: BEAM_MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the library runs
+ * on, held until the process ends (the real-shape layer fits up to about 400
+ * tokens).  The caller still passes inputs and outputs, as for beam_moe_forward.
+ *   Returns BEAM_MOE_ERR_WORKSPACE, before enqueuing anything, when
+ *   beam_moe_workspace_bytes(cfg, T, BEAM_MOE_OP_FORWARD) exceeds the array;
+ *   BEAM_MOE_ERR_HIP if the array's address on the current device cannot be
+ *   found (looked up once per device, with that device current, at the first
+ *   call there).  The kernels run on the device current at the call.
+ *   Every call on a device uses that device's one array: calls that overlap on
+ *   one device (other streams, other threads) race on it, so issue them in
+ *   order on one stream.  Nothing in the array needs to start at zero; it
+ *   keeps the last call's intermediates.
+ * Calls no hipMalloc, hipFree or allocating routine. */
+#define BEAM_MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int beam_moe_forward_noalloc(const beam_moe_config* cfg, int32_t T,
+                             const void* x, const float* w_router, const float* b_router,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* s_gate, const void* s_up, const void* s_down,
+                             void* out, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* RMSNorm of bf16 rows (the norm before and after every sublayer: Reflection
  * Beam 1.0 overview, section "Residual stream", which fixes the norms to FP32;
  * RMSNorm with a per-channel gain is the reading, the only norm the pages name):

@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     beam_dense_workspace_bytes,
     beam_moe_block_forward,
     beam_moe_forward,
+    beam_moe_forward_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     beam_moe_permute,
     beam_moe_rms_norm,
     beam_moe_route,

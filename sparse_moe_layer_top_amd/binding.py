@@ -86,6 +86,8 @@ def _load():
     lib.beam_moe_forward.restype = ctypes.c_int
     lib.beam_moe_forward_timed.argtypes = [cfgp, I32] + [P] * 13 + [SZ, P, P]
     lib.beam_moe_forward_timed.restype = ctypes.c_int
+    lib.beam_moe_forward_noalloc.argtypes = [cfgp, I32] + [P] * 13
+    lib.beam_moe_forward_noalloc.restype = ctypes.c_int
     F32 = ctypes.c_float
     lib.beam_moe_rms_norm.argtypes = [I32, I32, P, P, F32, P, P]
     lib.beam_moe_rms_norm.restype = ctypes.c_int
@@ -257,6 +259,35 @@ def beam_moe_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_rou
             raise ValueError("stage_events must be 7 torch.cuda.Event objects, each recorded once beforehand")
         arr = (ctypes.c_void_p * 7)(*[ev.cuda_event for ev in stage_events])
         _check("beam_moe_forward_timed", LIB.beam_moe_forward_timed(*args, arr))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def beam_moe_forward_noalloc(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor],
+                             w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                             out: torch.Tensor, s_gate: Optional[torch.Tensor] = None,
+                             s_up: Optional[torch.Tensor] = None, s_down: Optional[torch.Tensor] = None,
+                             topk_ids_out: Optional[torch.Tensor] = None,
+                             topk_w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """beam_moe_forward with the library's fixed device scratch array as its workspace (for callers that
+    cannot allocate): the caller passes every input and output, `out` included; nothing is allocated.
+    Calls on one device share the array, so they must not overlap."""
+    T, dev = x.shape[0], x.device
+    E, H, I = cfg.n_experts, cfg.hidden, cfg.inter
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(w_router, "w_router", torch.float32, (H, E), dev)
+    _need(b_router, "b_router", torch.float32, (E,), dev, optional=True)
+    _expert_weights(cfg.weight_type, (E,), H, I, w_gate, w_up, w_down, s_gate, s_up, s_down, dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    _need(topk_ids_out, "topk_ids_out", torch.int32, (T, cfg.top_k), dev, optional=True)
+    _need(topk_w_out, "topk_w_out", torch.float32, (T, cfg.top_k), dev, optional=True)
+    _check("beam_moe_forward_noalloc",
+           LIB.beam_moe_forward_noalloc(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(b_router),
+                                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up),
+                                        _ptr(s_down), _ptr(out), _ptr(topk_ids_out), _ptr(topk_w_out),
+                                        _stream(dev)))
     return out
 
 

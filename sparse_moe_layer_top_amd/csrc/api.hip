@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using beam::Layout;
@@ -319,6 +321,53 @@ int beam_moe_forward_timed(const beam_moe_config* cfg, int32_t T, const void* x,
   return run_forward(s, L, T, static_cast<const uint16_t*>(x), w_router, b_router, w_gate, w_up, w_down, s_gate, s_up,
                      s_down, static_cast<uint16_t*>(out), topk_ids_out, topk_w_out, workspace,
                      static_cast<hipStream_t>(stream), stage_events, nullptr);
+}
+
+// ---- allocation-free forward: the workspace is a fixed device array of this library ----
+// In host code `scratch` names the symbol only; kernels get its device address, looked up per device.
+static __device__ __align__(256) uint8_t scratch[BEAM_MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (each GPU holds its own), found once per device with that
+// device current and kept.
+int scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BEAM_MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_MOE_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return BEAM_MOE_OK;
+}
+}  // namespace
+
+int beam_moe_forward_noalloc(const beam_moe_config* cfg, int32_t T, const void* x, const float* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+                             const void* s_gate, const void* s_up, const void* s_down, void* out,
+                             int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  int st = check_config(cfg);
+  if (st != BEAM_MOE_OK) return st;
+  if (T < 0 || T > BEAM_MOE_MAX_TOKENS) return BEAM_MOE_ERR_INVALID;
+  if (T == 0) return BEAM_MOE_OK;
+  st = check_forward_args(cfg, x, w_router, b_router, w_gate, w_up, w_down, s_gate, s_up, s_down, out, topk_ids_out,
+                          topk_w_out);
+  if (st != BEAM_MOE_OK) return st;
+  const Shape s = shape_of(cfg);
+  const Layout L = make_layout(s, T, BEAM_MOE_OP_FORWARD);
+  if (L.total > BEAM_MOE_NOALLOC_SCRATCH_BYTES) return BEAM_MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BEAM_MOE_OK) return st;
+  return run_forward(s, L, T, static_cast<const uint16_t*>(x), w_router, b_router, w_gate, w_up, w_down, s_gate, s_up,
+                     s_down, static_cast<uint16_t*>(out), topk_ids_out, topk_w_out, ws,
+                     static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
 int beam_moe_rms_norm(int32_t T, int32_t hidden, const void* x, const float* gamma, float eps, void* out,

@@ -265,3 +265,23 @@ def test_binding_checks_mxfp4_shapes():
     sc = torch.empty(E, I, H // 32, dtype=torch.float32)
     with pytest.raises(TypeError, match="expected torch.uint8"):
         B._need(sc, "s_gate", torch.uint8, (E, I, H // 32))
+
+
+def test_noalloc_forward_validation():
+    """The allocation-free forward checks its arguments like the forward, and rejects a layer whose
+    workspace exceeds the fixed scratch array before enqueuing anything (or touching the GPU)."""
+    c = ctypes.byref(_cfg())
+    f = FAKE
+    assert B.LIB.beam_moe_forward_noalloc(c, 0, *([None] * 12), None) == B.OK
+    assert B.LIB.beam_moe_forward_noalloc(None, 4, *([f] * 12), None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_forward_noalloc(c, -1, *([f] * 12), None) == B.ERR_INVALID
+    # x missing; scales given for bf16 weights
+    assert B.LIB.beam_moe_forward_noalloc(c, 4, None, f, None, f, f, f, None, None, None, f, None, None, None) == B.ERR_INVALID
+    assert B.LIB.beam_moe_forward_noalloc(c, 4, f, f, None, f, f, f, f, f, f, f, None, None, None) == B.ERR_INVALID
+    # the scratch array's limit: the real-shape layer's forward workspace crosses 64 MiB between 256 and 512 tokens
+    cfg = bm.Config()
+    assert bm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    fits = [T for T in (1, 64, 128, 256, 512, 8192) if bm.beam_moe_workspace_bytes(cfg, T) <= bm.NOALLOC_SCRATCH_BYTES]
+    assert fits == [1, 64, 128, 256]
+    assert B.LIB.beam_moe_forward_noalloc(c, 512, f, f, None, f, f, f, None, None, None, f, None, None, None) == B.ERR_WORKSPACE
+    assert B.LIB.beam_moe_forward_noalloc(c, 8192, f, f, None, f, f, f, None, None, None, f, None, None, None) == B.ERR_WORKSPACE
