@@ -59,7 +59,9 @@ typedef enum {
  * (value 2^(e-127); codes 1..254), and each weight is an FP4 E2M1 code (values
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte with the
  * lower-indexed weight in the low nibble.  MXFP4 needs H and I to be multiples
- * of 256 and runs on the weight-streaming kernels at every T. */
+ * of 256.  It never takes the LDS-tiled GEMMs: it runs on the one-workgroup-
+ * per-CU GEMMs at 32 to 64 rows per expert on average and on the weight-
+ * streaming GEMMs otherwise. */
 typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1, BEAM_MOE_W_MXFP4 = 2 } beam_moe_wtype;
 
 typedef enum {

@@ -253,11 +253,12 @@ def test_real_shape_forward(name, n_sample):
 
 
 def test_real_shape_skew_tile_edges():
-    """Skewed routing at T = 8192: 256 rows per expert on average, so the gate/up GEMM runs one
-    workgroup per CU over 272-row tiles; the most loaded expert spans several tiles, others fall
-    just above 256 rows or hold a handful.  Ids and weights for every token; outputs for tokens at
-    row-tile edges (permuted rows 0, 255, 256, 271, 272, 543, 544 and the last of the most loaded
-    expert; the rows past 256 of an expert with 257..272; the least loaded expert's first row)."""
+    """Skewed routing at T = 8192: 256 rows per expert on average, so the GEMMs run one workgroup
+    per CU over row tiles; the most loaded expert spans many tiles, others fall just above 256 rows
+    or hold a handful.  Ids and weights for every token; outputs for tokens at row-tile edges (the
+    first row, and rows k*t - 1 and k*t for tile heights t of 144, 272 and 288 and k = 1..3, and the
+    last row of the most loaded expert; the rows past 256 of an expert with 257..272; the least
+    loaded expert's first row)."""
     w = gen.workload("skew", 8192)
     spec, x, wr, b = C.guarded(w, 0)
     W = real_weights("bf16")
@@ -272,7 +273,8 @@ def test_real_shape_skew_tile_edges():
 
     picks = []
     big = tokens_of(int(load.argmax()))
-    picks += [big[r] for r in (0, 255, 256, 271, 272, 543, 544) if r < len(big)] + [big[-1]]
+    edges = {0} | {k * t + d for t in (144, 272, 288) for k in (1, 2, 3) for d in (-1, 0)}
+    picks += [big[r] for r in sorted(edges) if r < len(big)] + [big[-1]]
     near = np.nonzero((load > 256) & (load <= 272))[0]
     if len(near):
         t = tokens_of(int(near[0]))
