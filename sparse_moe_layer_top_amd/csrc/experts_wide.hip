@@ -56,10 +56,11 @@
 //     contiguous ranges, so the workgroups of one expert share its
 //     activation rows in one L2.
 //
-// Balanced bf16 gate/up (272-row tiles, NB = 2): the MFMAs of a window read
-// one activation fragment per two MFMAs from LDS, which bounds the compute
-// phase at about 65% of the MFMA rate (measured for that mix alone); the
-// loads overlap it only in part.
+// Balanced bf16 gate/up (272-row tiles, NB = 2): the loads set the time.  A
+// window brings 34 KB of activation rows (L2 hits) per 32 KB of weights (HBM)
+// through each CU's vector memory path, whose address unit is then about 71%
+// busy; the MFMAs run about 53% of the kernel's cycles and are mostly hidden
+// behind the loads (timing variants without MFMAs are 6% faster).
 // At 96-row tiles (NB = 4) the work is HBM-bound: a window brings 12 KB of
 // activations and 64 KB (bf16) of weights per CU.
 #include <type_traits>
