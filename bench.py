@@ -174,9 +174,9 @@ def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, 
     out = torch.empty(w.T, w.hidden, dtype=torch.bfloat16, device=dev)
     ids = torch.empty(w.T, w.top_k, dtype=torch.int32, device=dev)
     wts = torch.empty(w.T, w.top_k, dtype=torch.float32, device=dev)
-    ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
-
     dense = w.n_experts == 1
+    if not dense:
+        ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
     stages = BLOCK_STAGES if block else (DENSE_STAGES if dense else STAGES)
     if dense:
         dcfg = bm.DenseConfig(w.hidden, w.inter, wtype)

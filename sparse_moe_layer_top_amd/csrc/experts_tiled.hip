@@ -44,10 +44,15 @@ constexpr int kXcds = 8;
 
 enum { kGateUp = 0, kDown = 1 };
 
-template <bool FP8>
+// NBW: weight-row blocks of 16 per column wave (4 waves): 4 (256 weight rows per tile) or, for the
+// bf16 down GEMM, 5 (320 output columns: each 64-k stage then brings 36 KB of h rows per 40 KB of
+// weights instead of per 32 KB, and its MFMAs take a quarter longer to cover the next stage's loads).
+template <bool FP8, int NBW = 4>
 struct TiledGeom {
+  static constexpr int NBLK = 4 * NBW;                   // weight-row blocks per tile
+  static constexpr int TN = 16 * NBLK;                   // weight rows per tile
   static constexpr int A_FR = kMBlk * 2;                 // A fragments per stage
-  static constexpr int B_FR = kNBlk * (FP8 ? 1 : 2);     // B fragments per stage
+  static constexpr int B_FR = NBLK * (FP8 ? 1 : 2);      // B fragments per stage
   static constexpr int FR = A_FR + B_FR;
   static constexpr int STAGE = FR * 1024;                // bytes per stage
   static constexpr int LPW = (FR + 7) / 8;               // fragment loads per wave per stage
@@ -59,7 +64,7 @@ __device__ __forceinline__ void load_lds16(const void* g, uint8_t* lds_wave_base
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
 }
 
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, int NBW>
 __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const uint16_t* __restrict__ act,
                                                     const void* __restrict__ w0, const void* __restrict__ w1,
                                                     const float* __restrict__ s0, const float* __restrict__ s1,
@@ -68,13 +73,16 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
                                                     const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
                                                     int tile_rows) {
-  using G = TiledGeom<FP8>;
-  constexpr int NC = MODE == kGateUp ? 128 : kTN;        // output columns per tile
+  using G = TiledGeom<FP8, NBW>;
+  static_assert(MODE == kDown || NBW == 4, "gate/up pairs 2 gate + 2 up blocks per wave");
+  constexpr int NC = MODE == kGateUp ? 128 : G::TN;      // output columns per tile
   constexpr int CST = NC * 2 + 16;                        // staged output row stride in bytes
-  constexpr int LDS = (2 * G::STAGE > kTM * CST) ? 2 * G::STAGE : kTM * CST;
+  // the output tile goes out in EP passes of kTM / EP rows when it does not fit the two stages
+  constexpr int EP = kTM * CST <= 2 * G::STAGE ? 1 : 2;
+  constexpr int LDS = (2 * G::STAGE > kTM / EP * CST) ? 2 * G::STAGE : kTM / EP * CST;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
-  const int NT = MODE == kGateUp ? I / 128 : H / kTN;     // column blocks per tile
+  const int NT = MODE == kGateUp ? I / 128 : H / G::TN;   // column blocks per tile
   const int KD = MODE == kGateUp ? H : I;                 // reduction length
   const int nitems = ntiles[0] * NT;
   const int per_xcd = (nitems + kXcds - 1) / kXcds;
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
         wrow = (size_t)e * I + jn * 128 + (nb % 8) * 16 + rib;
       } else {
         wbase = w0;
-        wrow = (size_t)e * H + jn * kTN + nb * 16 + rib;
+        wrow = (size_t)e * H + jn * G::TN + nb * 16 + rib;
       }
       const size_t k0 = FP8 ? (size_t)q * 16 : (size_t)(lchunk ^ j) * 8;
       src[i] = static_cast<const uint8_t*>(wbase) + (wrow * KD + k0) * WB;
@@ -141,17 +149,17 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
 #pragma unroll
   for (int a = 0; a < 2; ++a) roff[a] = (l16 / 8) * 1024 + ((l16 % 8) * 8 + ((2 * q + a) ^ (l16 % 8) ^ (l16 / 8))) * 16;
 
-  // this wave's weight-row blocks: gate/up pairs for the SwiGLU, or 4 down blocks
-  int nbs[4];
+  // this wave's weight-row blocks: gate/up pairs for the SwiGLU, or NBW down blocks
+  int nbs[NBW];
 #pragma unroll
-  for (int n = 0; n < 4; ++n)
-    nbs[n] = MODE == kGateUp ? ((n < 2) ? 2 * wn + n : 8 + 2 * wn + (n - 2)) : 4 * wn + n;
+  for (int n = 0; n < NBW; ++n)
+    nbs[n] = MODE == kGateUp ? ((n < 2) ? 2 * wn + n : 8 + 2 * wn + (n - 2)) : NBW * wn + n;
 
-  f32x4 acc[9][4];
+  f32x4 acc[9][NBW];
 #pragma unroll
   for (int m = 0; m < 9; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NBW; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kWaitLoads = (7 << 4) | (15 << 8);        // s_waitcnt vmcnt(0)
   const int nst = KD / kBK;
@@ -164,17 +172,17 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
     asm volatile("" ::: "memory");
     if (s + 1 < nst) issue(s + 1, buf ^ 1);
     const uint8_t* st = smem + buf * G::STAGE;
-    u32x4 braw[4];
+    u32x4 braw[NBW];
     if constexpr (FP8) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < NBW; ++n)
         braw[n] = *reinterpret_cast<const u32x4*>(st + (G::A_FR + nbs[n]) * 1024 + lane * 16);
     }
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      bf16x8 b[4];
+      bf16x8 b[NBW];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
+      for (int n = 0; n < NBW; ++n) {
         if constexpr (FP8) {
           b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{braw[n][0], braw[n][1]} : u32x2{braw[n][2], braw[n][3]});
         } else {
@@ -187,59 +195,68 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
         if (mb < nmb) {   // wave-uniform
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + mb * 2048 + roff[a]);
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
+          for (int n = 0; n < NBW; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
         }
       }
     }
   }
 
   // epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block; stage the bf16 tile
-  // row-major in LDS (every wave is done with the last stage first), then store whole rows
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  if constexpr (MODE == kGateUp) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int c = (2 * wn + n) * 16 + l16;
-      const float sg = FP8 ? s0[(size_t)e * I + jn * 128 + c] : 1.f;
-      const float su = FP8 ? s1[(size_t)e * I + jn * 128 + c] : 1.f;
-#pragma unroll
-      for (int m = 0; m < 9; ++m) {
-        if (wm * 9 + m < nmb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = (wm * 9 + m) * 16 + q * 4 + i;
-            const float g = acc[m][n][i] * sg, u = acc[m][n + 2][i] * su;
-            *reinterpret_cast<uint16_t*>(smem + r * CST + c * 2) = f32_to_bf16(silu(g) * u);
-          }
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = (4 * wn + n) * 16 + l16;
-      const float sd = FP8 ? s0[(size_t)e * H + jn * kTN + c] : 1.f;
-#pragma unroll
-      for (int m = 0; m < 9; ++m) {
-        if (wm * 9 + m < nmb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = (wm * 9 + m) * 16 + q * 4 + i;
-            *reinterpret_cast<uint16_t*>(smem + r * CST + c * 2) = f32_to_bf16(acc[m][n][i] * sd);
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
+  // row-major in LDS (every wave is done with the last stage first), then store whole rows; with
+  // EP = 2, the row half of waves wm = p goes out in pass p
   constexpr int CPR = NC / 8;                               // 16-byte chunks per output row
   const int ldo = MODE == kGateUp ? I : H;
   uint16_t* const obase = out + (size_t)(lo + r0) * ldo + (size_t)jn * NC;
-  for (int idx = threadIdx.x; idx < rows * CPR; idx += 512) {
-    const int r = idx / CPR, ch = idx % CPR;
-    *reinterpret_cast<u32x4*>(obase + (size_t)r * ldo + ch * 8) = *reinterpret_cast<const u32x4*>(smem + r * CST + ch * 16);
+#pragma unroll
+  for (int p = 0; p < EP; ++p) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int rbase = p * (kTM / EP);                      // first row staged in this pass
+    if (EP == 1 || wm == p) {
+      if constexpr (MODE == kGateUp) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int c = (2 * wn + n) * 16 + l16;
+          const float sg = FP8 ? s0[(size_t)e * I + jn * 128 + c] : 1.f;
+          const float su = FP8 ? s1[(size_t)e * I + jn * 128 + c] : 1.f;
+#pragma unroll
+          for (int m = 0; m < 9; ++m) {
+            if (wm * 9 + m < nmb) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = (wm * 9 + m) * 16 + q * 4 + i;
+                const float g = acc[m][n][i] * sg, u = acc[m][n + 2][i] * su;
+                *reinterpret_cast<uint16_t*>(smem + (r - rbase) * CST + c * 2) = f32_to_bf16(silu(g) * u);
+              }
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) {
+          const int c = (NBW * wn + n) * 16 + l16;
+          const float sd = FP8 ? s0[(size_t)e * H + jn * G::TN + c] : 1.f;
+#pragma unroll
+          for (int m = 0; m < 9; ++m) {
+            if (wm * 9 + m < nmb) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = (wm * 9 + m) * 16 + q * 4 + i;
+                *reinterpret_cast<uint16_t*>(smem + (r - rbase) * CST + c * 2) = f32_to_bf16(acc[m][n][i] * sd);
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int prow = min(rows - rbase, kTM / EP);           // rows of this pass that exist
+    for (int idx = threadIdx.x; idx < prow * CPR; idx += 512) {
+      const int r = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<u32x4*>(obase + (size_t)(rbase + r) * ldo + ch * 8) =
+          *reinterpret_cast<const u32x4*>(smem + r * CST + ch * 16);
+    }
   }
 }
 
@@ -266,10 +283,10 @@ hipError_t launch_gateup_tiled(const Shape& s, const uint16_t* x, const void* wg
   if (tile_rows < 1 || tile_rows > kTM) return hipErrorInvalidValue;
   const dim3 grid(grid_for(max_tiles, s.I / 128));
   if (s.fp8)
-    hipLaunchKernelGGL((tiled_kernel<kGateUp, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
+    hipLaunchKernelGGL((tiled_kernel<kGateUp, true, 4>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
                        offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
   else
-    hipLaunchKernelGGL((tiled_kernel<kGateUp, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
+    hipLaunchKernelGGL((tiled_kernel<kGateUp, false, 4>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
                        offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
   return hipGetLastError();
 }
@@ -278,13 +295,17 @@ hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, 
                              const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                              int tile_rows, uint16_t* y, hipStream_t stream) {
   if (tile_rows < 1 || tile_rows > kTM) return hipErrorInvalidValue;
-  const dim3 grid(grid_for(max_tiles, s.H / kTN));
-  if (s.fp8)
-    hipLaunchKernelGGL((tiled_kernel<kDown, true>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
-                       nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
-  else
-    hipLaunchKernelGGL((tiled_kernel<kDown, false>), grid, dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd,
-                       nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
+  if (s.fp8) {
+    hipLaunchKernelGGL((tiled_kernel<kDown, true, 4>), dim3(grid_for(max_tiles, s.H / kTN)), dim3(512), 0, stream,
+                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
+  } else if (s.H % TiledGeom<false, 5>::TN == 0) {
+    hipLaunchKernelGGL((tiled_kernel<kDown, false, 5>), dim3(grid_for(max_tiles, s.H / TiledGeom<false, 5>::TN)),
+                       dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
+                       ntiles, y, tile_rows);
+  } else {
+    hipLaunchKernelGGL((tiled_kernel<kDown, false, 4>), dim3(grid_for(max_tiles, s.H / kTN)), dim3(512), 0, stream,
+                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,27 @@
+"""bench.py's measurement on small workloads (the MoE forward, the whole sublayer, the dense MLP):
+each path runs, times its stages and reports its figures, so a change to the bench or the library's
+argument checks cannot leave one of the bench's workloads broken."""
+import numpy as np
+import pytest
+import torch
+
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,block", [("tiny", False), ("tiny", True), ("dense_tiny", False)])
+def test_measure_runs(name, block):
+    import bench
+    w = gen.workload(name)
+    dev = torch.device("cuda:0")
+    x, wr, b = gen.router_inputs(w, 0)
+    W = gen.device_expert_weights(w, 0, dev)
+    m = bench.measure(w, W, x, wr, b, steps=3, warmup=1, block=block)
+    assert m["ms_per_step"] > 0 and m["tokens_per_s"] > 0
+    stages = bench.BLOCK_STAGES if block else (bench.DENSE_STAGES if w.n_experts == 1 else bench.STAGES)
+    assert set(m["stage_ms"]) == set(stages)
+    assert all(np.isfinite(v) and v >= 0 for v in m["stage_ms"].values())
+    assert m["roofline"]["kernel"] and m["roofline"]["frac"] > 0
+    if w.n_experts > 1:
+        assert m["routing"]["touched_experts"] > 0

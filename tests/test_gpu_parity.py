@@ -121,6 +121,11 @@ ODD_SHAPES = [
     ("edge_above_64", 257, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
     ("edge_192_rows", 768, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
     ("edge_below_192", 767, 512, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    # the LDS-tiled down GEMM over 320-column tiles (H a multiple of 320 and 256): 288-row tiles from
+    # the tiled gate/up (about 150 rows per expert), and 272-row tiles from the one-workgroup-per-CU
+    # gate/up (about 375 rows per expert: two tiles each, the second ragged)
+    ("down320_tiled", 600, 1280, 256, 32, 8, 4, 8, 2.5, "bf16"),
+    ("down320_wide", 1500, 1280, 256, 32, 8, 4, 8, 2.5, "bf16"),
 ]
 
 
