@@ -161,6 +161,22 @@ def test_tiny_block_fp8():
     check_mix(out, s, moe, gpost, 4)
 
 
+@pytest.mark.parametrize("T", [64, 1100])
+def test_tiny_block_mxfp4(T):
+    """The whole sublayer with MXFP4 experts (streaming GEMMs at 64 tokens, the one-workgroup-per-CU
+    GEMMs at 1100 tokens: about 34 rows per expert)."""
+    w = gen.workload("tiny_mx", T)
+    C.say(f"[tiny_mx block] T={T}")
+    spec, s, wr, b, gpre, gpost = guarded_block(w, 6)
+    W, src = C.host_expert_weights(w, 6)
+    out, moe, ids, wts = run_block(w, s, wr, b, gpre, gpost, W, 7)
+    ref = oracle.block_forward(spec, s, gpre, gpost, EPS, 7, wr, b, src.get)
+    check_block_routing(spec, s, wr, b, gpre, ids, wts)
+    C.check_out(moe, ref["out"], what="MoE output")
+    C.check_out(out, ref["stream_out"], what="new stream")
+    check_mix(out, s, moe, gpost, 7)
+
+
 @pytest.mark.parametrize("name,n_sample", [("decode", 8), ("prefill", 16)])
 def test_real_shape_block(name, n_sample):
     from tests.test_gpu_parity import real_source, real_weights
