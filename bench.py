@@ -159,15 +159,16 @@ def gateup_kind(w):
     return "wide" if wide else ("tiled" if tiled else "stream")
 
 
-def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, seed=0):
-    """Time `steps` forward passes of workload w on resident inputs; returns the workload's figures."""
+def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, seed=0, layout=1):
+    """Time `steps` forward passes of workload w on resident inputs (expert weights W in row order,
+    layout 0, or fragment order, layout 1); returns the workload's figures."""
     import torch
     import sparse_moe_layer_top_amd as bm
     from synth import gen
 
     dev = torch.device("cuda:0")
     wtype = {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight]
-    cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha, wtype)
+    cfg = bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha, wtype, layout)
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     wr_t = torch.from_numpy(wr).to(dev)
     b_t = torch.from_numpy(b).to(dev)
@@ -179,7 +180,7 @@ def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, 
         ws = torch.empty(bm.beam_moe_workspace_bytes(cfg, w.T), dtype=torch.uint8, device=dev)
     stages = BLOCK_STAGES if block else (DENSE_STAGES if dense else STAGES)
     if dense:
-        dcfg = bm.DenseConfig(w.hidden, w.inter, wtype)
+        dcfg = bm.DenseConfig(w.hidden, w.inter, wtype, layout)
         Wd = {k: v[0] for k, v in W.items()}
         ws = torch.empty(max(1, bm.beam_dense_workspace_bytes(dcfg, w.T)), dtype=torch.uint8, device=dev)
     if block:
@@ -338,6 +339,9 @@ def main():
                          "(beam_moe_block_forward, step 23 = layer 10's MoE sublayer)")
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without the per-stage events (no roofline entry)")
+    ap.add_argument("--weight-order", default="fragments", choices=["fragments", "rows"],
+                    help="byte order of the expert weights in HBM: fragment order (written once by "
+                         "beam_moe_pack_weights before timing; the default) or row order")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -373,8 +377,15 @@ def main():
     t0 = time.time()
     W = gen.device_expert_weights(w, args.seed, dev, log=log)
     log(f"[bench] expert weights on device in {time.time() - t0:.1f} s")
+    layout = 1 if args.weight_order == "fragments" else 0
+    if layout:
+        import sparse_moe_layer_top_amd as bm
+        for k in ("gate", "up", "down"):       # one matrix stack at a time: one extra copy at most
+            W[k] = bm.beam_moe_pack_weights(W[k])
+            torch.cuda.synchronize()
+        log("[bench] expert weights packed into fragment order")
     m = measure(w, W, x_bits, wr, b, steps, warmup, block=args.block, stage_events=not args.no_stage_events,
-                seed=args.seed)
+                seed=args.seed, layout=layout)
 
     res = {
         "metric": METRIC, "value": m["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
@@ -382,7 +393,8 @@ def main():
         "vs_baseline": None, "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 MFMA",
                                        "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 MFMA"}[w.weight],
         "data": "synthetic (seeded, random-init weights of the real layer shape)",
-        "config": {"workload": describe(w, args.block), "T": w.T, "weights": w.weight, "bias": w.bias},
+        "config": {"workload": describe(w, args.block), "T": w.T, "weights": w.weight, "bias": w.bias,
+                   "weight_order": args.weight_order},
     }
     res.update({k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")})
     if not args.no_cpu_baseline:
@@ -395,7 +407,8 @@ def main():
         assert wp.weights_id == w.weights_id and wp.weight == w.weight
         psteps, pwarm = DEFAULTS["prefill"]
         px, pwr, pb = gen.router_inputs(wp, args.seed)
-        pm = measure(wp, W, px, pwr, pb, psteps, pwarm, stage_events=not args.no_stage_events, seed=args.seed)
+        pm = measure(wp, W, px, pwr, pb, psteps, pwarm, stage_events=not args.no_stage_events, seed=args.seed,
+                     layout=layout)
         pref = {"workload": describe(wp), "T": wp.T, "bias": wp.bias, "steps": psteps, "warmup": pwarm,
                 "target": {"ms_per_step": 4.10, "mfma_frac": 0.5}}
         pref.update(pm)

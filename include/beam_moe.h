@@ -22,7 +22,8 @@
  *     The caller owns every buffer; the library allocates nothing and keeps no
  *     state between calls.  Device pointers must be 16-byte aligned.
  *   - Matrices are row-major.  Expert weights are stored [E, out, in]: the
- *     reduction dimension is contiguous.  bf16 tensors are passed as raw
+ *     reduction dimension is contiguous, in row order or, when the config asks
+ *     for it, in fragment order (beam_moe_wlayout below).  bf16 tensors are passed as raw
  *     16-bit patterns, e4m3 tensors as raw bytes (OCP e4m3fn: bias 7, max 448,
  *     S.1111.111 = NaN).
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
@@ -64,6 +65,20 @@ typedef enum {
  * streaming GEMMs otherwise. */
 typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1, BEAM_MOE_W_MXFP4 = 2 } beam_moe_wtype;
 
+/* Byte order of the expert weight matrices (the FP8 and MXFP4 scales always stay in row order).
+ * The pages fix no storage order; these are two orders of the same bytes, and a forward gives
+ * bit-identical results with either.
+ *   ROWS       [E, out, in] as described with each entry point: every row's bytes contiguous.
+ *   FRAGMENTS  each expert matrix, taken as R rows of B bytes (B = 2*in for bf16, in for e4m3,
+ *              in/2 for MXFP4 codes), is cut into blocks of 16 consecutive rows, and each block
+ *              into 64-byte column slices.  Slice f of block b is stored as 1024 contiguous bytes
+ *              at byte 16*B*b + 1024*f of the matrix, whose byte 16*(r + 16*c) + j holds byte
+ *              64*f + 16*c + j of the block's row r (r < 16, c < 4, j < 16).  That is the order
+ *              in which the 64 lanes of a wavefront take a 16 x 16 x 32 matrix-core operand, so
+ *              one 16-byte load per lane reads 1 KB of consecutive addresses.  The matrix keeps
+ *              its size; beam_moe_pack_weights writes this order from row order. */
+typedef enum { BEAM_MOE_LAYOUT_ROWS = 0, BEAM_MOE_LAYOUT_FRAGMENTS = 1 } beam_moe_wlayout;
+
 typedef enum {
   BEAM_MOE_OP_ROUTE = 0,
   BEAM_MOE_OP_PERMUTE = 1,
@@ -83,6 +98,7 @@ typedef struct {
   int32_t top_k;        /* K: 1..8, K <= Gk * E / G */
   float routed_scale;   /* alpha: finite */
   int32_t weight_type;  /* beam_moe_wtype */
+  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down */
 } beam_moe_config;
 
 /* Largest T accepted by every entry point. */
@@ -256,6 +272,7 @@ typedef struct {
   int32_t hidden;       /* H: multiple of 128 (256 for MXFP4) */
   int32_t inter;        /* I: multiple of 128 (256 for MXFP4) */
   int32_t weight_type;  /* beam_moe_wtype */
+  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down */
 } beam_dense_config;
 
 /* Workspace bytes of beam_dense_mlp_forward for T tokens (host only, pure): the
@@ -297,6 +314,16 @@ int beam_dense_mlp_forward_timed(const beam_dense_config* cfg, int32_t T, const 
  * Returns BEAM_MOE_ERR_INVALID for a bad size, a NULL or misaligned pointer.
  * Integer and compare operations only: the result is exact and reproducible. */
 int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, void* scales, void* stream);
+
+/* Row order -> fragment order (BEAM_MOE_LAYOUT_FRAGMENTS above) of a weight matrix, or of all
+ * E expert matrices of one kind at once (they are consecutive blocks of rows).
+ *   rows       R: a multiple of 16 (E*I for w_gate/w_up, E*H for w_down)
+ *   row_bytes  B: a multiple of 64 (2*in for bf16, in for e4m3, in/2 for MXFP4 codes)
+ *   src        [device] R*B bytes in row order, 16-byte aligned
+ *   dst        [device] R*B bytes out in fragment order, 16-byte aligned; must not overlap src
+ * rows == 0 is a no-op.  Returns BEAM_MOE_ERR_INVALID for a bad size, a NULL or misaligned
+ * pointer, or overlapping buffers.  A byte permutation: exact. */
+int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     BeamMoeError,
     Config,
     DenseConfig,
+    LAYOUT_FRAGMENTS,
+    LAYOUT_ROWS,
     LIB_PATH,
     MAX_NORM_HIDDEN,
     MAX_TOKENS,
@@ -26,6 +28,7 @@ from .binding import (  # noqa: F401
     beam_moe_forward,
     beam_moe_forward_noalloc,
     NOALLOC_SCRATCH_BYTES,
+    beam_moe_pack_weights,
     beam_moe_permute,
     beam_moe_rms_norm,
     beam_moe_route,

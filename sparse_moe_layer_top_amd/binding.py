@@ -18,6 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbeam_mo
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 W_BF16, W_FP8_E4M3, W_MXFP4 = 0, 1, 2
+LAYOUT_ROWS, LAYOUT_FRAGMENTS = 0, 1
 OP_ROUTE, OP_PERMUTE, OP_FORWARD, OP_BLOCK = 0, 1, 2, 3
 MAX_TOKENS = 262144
 MAX_NORM_HIDDEN = 8192
@@ -32,12 +33,13 @@ class BeamMoeError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float), ("weight_type", ctypes.c_int32)]
+                ("routed_scale", ctypes.c_float), ("weight_type", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
 class Config:
-    """Layer shape: hidden H, inter I, E experts in G groups, keep Gk groups, top-K, scale alpha."""
+    """Layer shape: hidden H, inter I, E experts in G groups, keep Gk groups, top-K, scale alpha; the
+    expert weights' type and byte order (LAYOUT_FRAGMENTS: as beam_moe_pack_weights writes them)."""
     hidden: int = 5120
     inter: int = 2560
     n_experts: int = 256
@@ -46,14 +48,16 @@ class Config:
     top_k: int = 8
     routed_scale: float = 2.5
     weight_type: int = W_BF16
+    weight_layout: int = LAYOUT_ROWS
 
     def c(self) -> _Config:
         return _Config(self.hidden, self.inter, self.n_experts, self.n_groups, self.topk_groups, self.top_k,
-                       self.routed_scale, self.weight_type)
+                       self.routed_scale, self.weight_type, self.weight_layout)
 
 
 class _DenseConfig(ctypes.Structure):
-    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("weight_type", ctypes.c_int32)]
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("weight_type", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -62,9 +66,10 @@ class DenseConfig:
     hidden: int = 5120
     inter: int = 20480
     weight_type: int = W_BF16
+    weight_layout: int = LAYOUT_ROWS
 
     def c(self) -> _DenseConfig:
-        return _DenseConfig(self.hidden, self.inter, self.weight_type)
+        return _DenseConfig(self.hidden, self.inter, self.weight_type, self.weight_layout)
 
 
 def _load():
@@ -104,6 +109,8 @@ def _load():
     lib.beam_dense_mlp_forward_timed.restype = ctypes.c_int
     lib.beam_mxfp4_quantize.argtypes = [I32, I32, P, P, P, P]
     lib.beam_mxfp4_quantize.restype = ctypes.c_int
+    lib.beam_moe_pack_weights.argtypes = [ctypes.c_int64, I32, P, P, P]
+    lib.beam_moe_pack_weights.restype = ctypes.c_int
     return lib
 
 
@@ -407,3 +414,25 @@ def beam_mxfp4_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
     _check("beam_mxfp4_quantize", LIB.beam_mxfp4_quantize(rows, cols, _ptr(w), _ptr(codes), _ptr(scales),
                                                           _stream(dev)))
     return codes, scales
+
+
+def beam_moe_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fragment order of weight matrices w [..., rows, cols] (bf16, or uint8 for e4m3 and MXFP4 codes):
+    the same shape and dtype with the bytes permuted as LAYOUT_FRAGMENTS describes (16-row blocks,
+    1 KB lane-ordered 64-byte column slices).  All leading rows are taken together: a multiple of 16,
+    each row a multiple of 64 bytes."""
+    if w.dim() < 2:
+        raise ValueError("w must have at least two dimensions")
+    if w.dtype not in (torch.bfloat16, torch.uint8):
+        raise ValueError(f"w must be bfloat16 or uint8, got {w.dtype}")
+    row_bytes = w.shape[-1] * w.element_size()
+    rows = w.numel() // w.shape[-1] if w.shape[-1] else 0
+    if rows % 16 or row_bytes % 64 or row_bytes == 0:
+        raise ValueError(f"rows ({rows}) must be a multiple of 16 and row bytes ({row_bytes}) of 64")
+    dev = w.device
+    _need(w, "w", w.dtype, tuple(w.shape))
+    if out is None:
+        out = torch.empty_like(w)
+    _need(out, "out", w.dtype, tuple(w.shape), dev)
+    _check("beam_moe_pack_weights", LIB.beam_moe_pack_weights(rows, row_bytes, _ptr(w), _ptr(out), _stream(dev)))
+    return out

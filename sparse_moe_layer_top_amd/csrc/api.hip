@@ -34,6 +34,8 @@ int check_config(const beam_moe_config* c) {
   if (!isfinite(c->routed_scale)) return BEAM_MOE_ERR_INVALID;
   if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3 && c->weight_type != BEAM_MOE_W_MXFP4)
     return BEAM_MOE_ERR_INVALID;
+  if (c->weight_layout != BEAM_MOE_LAYOUT_ROWS && c->weight_layout != BEAM_MOE_LAYOUT_FRAGMENTS)
+    return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->n_experts > beam::kMaxExperts || c->n_groups > 64 || c->top_k > beam::kMaxTopK)
@@ -45,6 +47,7 @@ Shape shape_of(const beam_moe_config* c) {
   Shape s{c->hidden, c->inter, c->n_experts, c->n_groups, c->topk_groups, c->top_k, c->routed_scale,
           c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
   s.mx = c->weight_type == BEAM_MOE_W_MXFP4;
+  s.packed = c->weight_layout == BEAM_MOE_LAYOUT_FRAGMENTS;
   return s;
 }
 
@@ -184,6 +187,8 @@ int check_dense_config(const beam_dense_config* c) {
   if (!c || c->hidden <= 0 || c->inter <= 0) return BEAM_MOE_ERR_INVALID;
   if (c->weight_type != BEAM_MOE_W_BF16 && c->weight_type != BEAM_MOE_W_FP8_E4M3 && c->weight_type != BEAM_MOE_W_MXFP4)
     return BEAM_MOE_ERR_INVALID;
+  if (c->weight_layout != BEAM_MOE_LAYOUT_ROWS && c->weight_layout != BEAM_MOE_LAYOUT_FRAGMENTS)
+    return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;
@@ -193,6 +198,7 @@ Shape dense_shape(const beam_dense_config* c) {
   Shape s{c->hidden, c->inter, 1, 1, 1, 1, 1.0f, c->weight_type == BEAM_MOE_W_FP8_E4M3 ? 1 : 0};
   s.dense = 1;
   s.mx = c->weight_type == BEAM_MOE_W_MXFP4;
+  s.packed = c->weight_layout == BEAM_MOE_LAYOUT_FRAGMENTS;
   return s;
 }
 
@@ -488,6 +494,19 @@ int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, 
   if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return BEAM_MOE_ERR_INVALID;
   BEAM_TRY_HIP(beam::launch_mxfp4_quantize(rows, cols, static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
                                            static_cast<uint8_t*>(scales), static_cast<hipStream_t>(stream)));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream) {
+  if (rows < 0 || rows % 16 != 0 || row_bytes <= 0 || row_bytes % 64 != 0) return BEAM_MOE_ERR_INVALID;
+  if (rows > (int64_t)1 << 40 || (int64_t)row_bytes > ((int64_t)1 << 40) / (rows ? rows : 1))
+    return BEAM_MOE_ERR_INVALID;
+  if (rows == 0) return BEAM_MOE_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return BEAM_MOE_ERR_INVALID;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)rows * (uintptr_t)row_bytes;
+  if (a < b + n && b < a + n) return BEAM_MOE_ERR_INVALID;
+  BEAM_TRY_HIP(beam::launch_pack_weights(rows, row_bytes, src, dst, static_cast<hipStream_t>(stream)));
   return BEAM_MOE_OK;
 }
 

@@ -91,8 +91,9 @@ struct AWin {
 // The streaming k-loop shared by both kernels.  A step covers SK k-values.
 // Lane (row/column l%16, quad q = l/16) owns k in [step*SK + q*SK/4, +SK/4):
 // one 16-byte weight load per weight block (NB blocks of 16 output columns)
-// per step; wrow/arow already include the lane's quad offset, srow (MXFP4) is
-// the row's scale base.
+// per step, wst weight elements after the last (row order: the next 64 bytes
+// of the row; fragment order: the block's next 1 KB slice); wrow/arow already
+// include the lane's offset, srow (MXFP4) is the row's scale base.
 //
 // Weights go straight from HBM into registers in bursts: a window of D steps
 // is issued back to back (each weight row sees D*64 contiguous bytes requested
@@ -106,12 +107,13 @@ struct AWin {
 // the weight ring, which sets how many bytes each CU keeps in flight.
 // sched_barrier fences keep the compiler from reordering the bursts.
 template <int WT, int MT, int NB, int D>
-__device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const typename WFrag<WT>::E* const (&wrow)[NB],
+__device__ __forceinline__ void stream_k(int nsteps, int wst, int wave, int lane,
+                                         const typename WFrag<WT>::E* const (&wrow)[NB],
                                          const uint8_t* const (&srow)[NB], const uint16_t* const (&arow)[MT],
                                          u32x4 (*lds)[AWin<WT, MT, D>::SLOTS][kWave], f32x4 (&acc)[MT][NB]) {
   using W = WFrag<WT>;
   using A = AWin<WT, MT, D>;
-  constexpr int SK = W::SK, SE = W::SE, NA = A::NA;
+  constexpr int SK = W::SK, NA = A::NA;
   const int q = lane / 16;
   const uint16_t* mine[A::FW];   // this lane's address of each fragment this wave loads (window 0)
 #pragma unroll
@@ -134,7 +136,7 @@ __device__ __forceinline__ void stream_k(int nsteps, int wave, int lane, const t
 #pragma unroll
     for (int j = 0; j < D; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (base + j) * SE);
+      for (int nb = 0; nb < NB; ++nb) wb[buf][j][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + (size_t)(base + j) * wst);
     if constexpr (W::kBlockScale) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
                                                             const int32_t* __restrict__ tiles,
                                                             const int32_t* __restrict__ ntiles,
                                                             uint16_t* __restrict__ h, int kparts, int nrows,
-                                                            float* __restrict__ part) {
+                                                            float* __restrict__ part, int packed) {
   using W = WFrag<WT>;
   __shared__ u32x4 lds[2][AWin<WT, MT, D>::SLOTS][kWave];
   const int tile = blockIdx.y;
@@ -265,12 +267,14 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
     xr[mt] = x + (size_t)tok * H + qa + zs * W::SK;
   }
   using WE = typename W::E;
+  const size_t HE = (size_t)H * W::SE / W::SK;          // a weight row in E units
   const WE* wr[2 * G];
   const uint8_t* sr[2 * G];
 #pragma unroll
   for (int g = 0; g < 2 * G; ++g) {
-    const size_t row = (size_t)e * I + col0 + (g % G) * 16 + l16;
-    wr[g] = static_cast<const WE*>(g < G ? wg : wu) + row * ((size_t)H * W::SE / W::SK) + qw + zs * W::SE;
+    const size_t row0 = (size_t)e * I + col0 + (g % G) * 16, row = row0 + l16;   // the block's first row, the lane's
+    wr[g] = static_cast<const WE*>(g < G ? wg : wu) +
+            (packed ? row0 * HE + lane * (16 / sizeof(WE)) + zs * W::SE * 16 : row * HE + qw + zs * W::SE);
     sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) + row * (H / 32) + zs * (W::SK / 32)
                            : nullptr;
   }
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2 * G, D>(nsteps, wave, lane, wr, sr, xr, lds, acc);
+  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, wave, lane, wr, sr, xr, lds, acc);
   if (!active) return;
   if (kparts > 1) {   // raw fp32 sums of this part: gate at part[z][row][col], up at part[z][row][I + col]
 #pragma unroll
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
                                                           const int32_t* __restrict__ tiles,
                                                           const int32_t* __restrict__ ntiles,
                                                           uint16_t* __restrict__ y, int kparts, int nrows,
-                                                          float* __restrict__ part) {
+                                                          float* __restrict__ part, int packed) {
   using W = WFrag<WT>;
   __shared__ u32x4 lds[2][AWin<WT, MT, D>::SLOTS][kWave];
   const int tile = blockIdx.y;
@@ -360,8 +364,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
   const uint8_t* sr[2 * G];
 #pragma unroll
   for (int g = 0; g < 2 * G; ++g) {
-    const size_t row = (size_t)e * H + c0 + g * 16 + l16;
-    wr[g] = static_cast<const WE*>(wd) + row * IE + qw + zs * W::SE;
+    const size_t row0 = (size_t)e * H + c0 + g * 16, row = row0 + l16;
+    wr[g] = static_cast<const WE*>(wd) +
+            (packed ? row0 * IE + lane * (16 / sizeof(WE)) + zs * W::SE * 16 : row * IE + qw + zs * W::SE);
     sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(sd) + row * (I / 32) + zs * (W::SK / 32) : nullptr;
   }
   f32x4 acc[MT][2 * G];
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2 * G, D>(nsteps, wave, lane, wr, sr, hr, lds, acc);
+  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, wave, lane, wr, sr, hr, lds, acc);
   if (!active) return;
 
 #pragma unroll
@@ -421,7 +426,7 @@ static hipError_t gateup_launch(const Shape& s, const uint16_t* x, const void* w
                                 int kparts, int nrows, float* part, hipStream_t stream) {
   hipLaunchKernelGGL((gateup_stream_kernel<WT, MT, G, D>), dim3((s.I + 64 * G - 1) / (64 * G), max_tiles, kparts),
                      dim3(256), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su, offsets, sorted_pairs, tiles, ntiles, h,
-                     kparts, nrows, part);
+                     kparts, nrows, part, s.packed);
   return hipGetLastError();
 }
 
@@ -466,7 +471,8 @@ static hipError_t down_launch(const Shape& s, const uint16_t* h, const void* wd,
                               const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                               uint16_t* y, int kparts, int nrows, float* part, hipStream_t stream) {
   hipLaunchKernelGGL((down_stream_kernel<WT, MT, G, D>), dim3((s.H + 128 * G - 1) / (128 * G), max_tiles, kparts),
-                     dim3(256), 0, stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part);
+                     dim3(256), 0, stream, s.H, s.I, h, wd, sd, offsets, tiles, ntiles, y, kparts, nrows, part,
+                     s.packed);
   return hipGetLastError();
 }
 

@@ -21,7 +21,10 @@
 //     natural fragment order, touches twice the cache lines and halves the
 //     rate at which a CU's loads complete.)  FP8 weights keep 16 e4m3 bytes
 //     per lane (both halves, 16 rows x 64 bytes) and are converted to bf16
-//     when read from LDS; the k mapping is the same.
+//     when read from LDS; the k mapping is the same.  Weights in fragment
+//     order (1 KB lane-ordered 64-byte column slices of 16-row blocks) arrive
+//     as whole slices, 1 KB of consecutive addresses per instruction, and land
+//     in LDS in that order: a bf16 lane reads chunk 2(q%2) + a of slice q/2.
 //   * Two LDS stages: stage s+1 streams in while stage s feeds the MFMAs.
 //   * 8 waves as 2 (rows) x 4 (columns); a wave owns 9 row blocks x 4 column
 //     blocks of 16x16x32 MFMA accumulators.  Row blocks past the tile's rows
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
                                                     const int32_t* __restrict__ sorted_pairs,
                                                     const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
-                                                    int tile_rows) {
+                                                    int tile_rows, int packed) {
   using G = TiledGeom<FP8, NBW>;
   static_assert(MODE == kDown || NBW == 4, "gate/up pairs 2 gate + 2 up blocks per wave");
   constexpr int NC = MODE == kGateUp ? 128 : G::TN;      // output columns per tile
@@ -120,34 +123,45 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
     } else {
       const int fb = f - G::A_FR;
       const int nb = FP8 ? fb : fb / 2, j = FP8 ? 0 : fb % 2;
-      const int rib = FP8 ? l16 : j * 8 + lrow;            // row inside the 16-row weight block
       const void* wbase;
-      size_t wrow;
+      size_t wrow0;                                        // the 16-row weight block's first row
       if (MODE == kGateUp) {
         wbase = nb < 8 ? w0 : w1;
-        wrow = (size_t)e * I + jn * 128 + (nb % 8) * 16 + rib;
+        wrow0 = (size_t)e * I + jn * 128 + (nb % 8) * 16;
       } else {
         wbase = w0;
-        wrow = (size_t)e * H + jn * G::TN + nb * 16 + rib;
+        wrow0 = (size_t)e * H + jn * G::TN + nb * 16;
       }
-      const size_t k0 = FP8 ? (size_t)q * 16 : (size_t)(lchunk ^ j) * 8;
-      src[i] = static_cast<const uint8_t*>(wbase) + (wrow * KD + k0) * WB;
+      if (packed) {   // slice j of the block's stage (bf16: two 64-byte slices per 128-byte stage)
+        src[i] = static_cast<const uint8_t*>(wbase) + wrow0 * KD * WB + j * 1024 + lane * 16;
+      } else {
+        const int rib = FP8 ? l16 : j * 8 + lrow;            // row inside the 16-row weight block
+        const size_t k0 = FP8 ? (size_t)q * 16 : (size_t)(lchunk ^ j) * 8;
+        src[i] = static_cast<const uint8_t*>(wbase) + ((wrow0 + rib) * KD + k0) * WB;
+      }
     }
   }
+  // bytes between stages: activation rows and row-order weights advance along the row; fragment-order
+  // weights by the 16 rows' stage slices
+  const size_t wstep = packed ? (size_t)16 * kBK * WB : (size_t)kBK * WB;
   auto issue = [&](int stage, int buf) {
 #pragma unroll
     for (int i = 0; i < G::LPW; ++i) {
       if (!on[i]) continue;   // wave-uniform
       const int f = wave + 8 * i;
-      const size_t step = (size_t)stage * kBK * (f < G::A_FR ? 2 : WB);
+      const size_t step = (size_t)stage * (f < G::A_FR ? kBK * 2 : wstep);
       load_lds16(src[i] + step, smem + buf * G::STAGE + f * 1024);
     }
   };
 
-  // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB load instructions)
-  int roff[2];
+  // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB load instructions), and
+  // its bf16 weight operand of half a (row order: the same; fragment order: chunk 2(q%2) + a of slice q/2)
+  int roff[2], wro[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) roff[a] = (l16 / 8) * 1024 + ((l16 % 8) * 8 + ((2 * q + a) ^ (l16 % 8) ^ (l16 / 8))) * 16;
+  for (int a = 0; a < 2; ++a) {
+    roff[a] = (l16 / 8) * 1024 + ((l16 % 8) * 8 + ((2 * q + a) ^ (l16 % 8) ^ (l16 / 8))) * 16;
+    wro[a] = packed ? (q / 2) * 1024 + (l16 + 16 * (2 * (q % 2) + a)) * 16 : roff[a];
+  }
 
   // this wave's weight-row blocks: gate/up pairs for the SwiGLU, or NBW down blocks
   int nbs[NBW];
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(512) void tiled_kernel(int H, int I, int K, const u
         if constexpr (FP8) {
           b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{braw[n][0], braw[n][1]} : u32x2{braw[n][2], braw[n][3]});
         } else {
-          b[n] = *reinterpret_cast<const bf16x8*>(st + (G::A_FR + nbs[n] * 2) * 1024 + roff[a]);
+          b[n] = *reinterpret_cast<const bf16x8*>(st + (G::A_FR + nbs[n] * 2) * 1024 + wro[a]);
         }
       }
 #pragma unroll
@@ -284,10 +298,10 @@ hipError_t launch_gateup_tiled(const Shape& s, const uint16_t* x, const void* wg
   const dim3 grid(grid_for(max_tiles, s.I / 128));
   if (s.fp8)
     hipLaunchKernelGGL((tiled_kernel<kGateUp, true, 4>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
-                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
+                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows, s.packed);
   else
     hipLaunchKernelGGL((tiled_kernel<kGateUp, false, 4>), grid, dim3(512), 0, stream, s.H, s.I, s.K, x, wg, wu, sg, su,
-                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows);
+                       offsets, sorted_pairs, tiles, ntiles, h, tile_rows, s.packed);
   return hipGetLastError();
 }
 
@@ -297,14 +311,16 @@ hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, 
   if (tile_rows < 1 || tile_rows > kTM) return hipErrorInvalidValue;
   if (s.fp8) {
     hipLaunchKernelGGL((tiled_kernel<kDown, true, 4>), dim3(grid_for(max_tiles, s.H / kTN)), dim3(512), 0, stream,
-                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
+                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows,
+                       s.packed);
   } else if (s.H % TiledGeom<false, 5>::TN == 0) {
     hipLaunchKernelGGL((tiled_kernel<kDown, false, 5>), dim3(grid_for(max_tiles, s.H / TiledGeom<false, 5>::TN)),
                        dim3(512), 0, stream, s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
-                       ntiles, y, tile_rows);
+                       ntiles, y, tile_rows, s.packed);
   } else {
     hipLaunchKernelGGL((tiled_kernel<kDown, false, 4>), dim3(grid_for(max_tiles, s.H / kTN)), dim3(512), 0, stream,
-                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows);
+                       s.H, s.I, s.K, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles, ntiles, y, tile_rows,
+                       s.packed);
   }
   return hipGetLastError();
 }

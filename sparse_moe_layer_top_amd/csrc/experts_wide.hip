@@ -33,7 +33,11 @@
 //     buffer's end (zeros, without a memory access) into one spare slot.
 //   * Lane (r = l%16, q = l/16) of MFMA half a of a window uses k in
 //     [16q + 8a, +8) of the window for both operands (fp8: the lane's 16
-//     weight bytes are k [16q, 16q + 16), half a the a-th 8 of them).
+//     weight bytes are k [16q, 16q + 16), half a the a-th 8 of them).  With
+//     the weights in fragment order (1 KB lane-ordered 64-byte column slices
+//     of 16-row blocks) a load instruction reads 8 whole 128-byte lines
+//     (bf16: four 256-byte runs; fp8, MXFP4: one 1 KB slice) instead of 16
+//     rows x 64 bytes.
 //     MXFP4 windows are 128 deep: lane q's 16 code bytes are k [32q, +32),
 //     one scale block, and MFMA slice t uses k [32q + 8t, +8); the
 //     activations sit as two 64-deep halves, so the lane reads half q/2,
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                                                    const int32_t* __restrict__ sorted_pairs,
                                                    const int32_t* __restrict__ tiles,
                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
-                                                   long act_bytes, int tgroup) {
+                                                   long act_bytes, int tgroup, int packed) {
   using C = WideCfg<WT, MODE, MT, NB>;
   constexpr int GPW = C::GPW;
   constexpr bool FP8 = WT == kWtFP8, MX = WT == kWtMX;
@@ -193,7 +197,14 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                        : wr0;
   constexpr int WCOLS = MODE == kWGateUp ? 8 * NB : 16 * NB;   // this wave's output columns
   const int wc0 = jn * C::COLS + wave * WCOLS;
-  const uint32_t woff = (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
+  // The lane's 16 bytes of a window.  Row order: row wc0 + l16, bf16 bytes [32q + 16a, +16) of the window
+  // (half a), fp8 and MXFP4 bytes [16q, +16).  Fragment order (a window is one 1 KB slice per 64 bytes of
+  // row, chunk c of row r at 16(r + 16c)): bf16 slice q/2, chunk 2(q%2) + a; fp8, MXFP4 chunk q.
+  const uint32_t woff = packed ? (uint32_t)wc0 * rowb + (WT == kWtBF16 ? (q / 2) * 1024 + (q % 2) * 512 + l16 * 16
+                                                                       : lane * 16)
+                               : (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
+  const int wwin = packed ? 16 * C::WIN_BYTES : C::WIN_BYTES;   // bytes between windows
+  const int whalf = packed ? 256 : 16;                          // bytes between a bf16 window's two loads
   const int bstride = 16 * rowb;         // bytes between blocks of 16 weight rows
   // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB groups)
   // (MXFP4: chunk 4(q%2) + t of the lane's half q/2, t = 0..3)
@@ -263,17 +274,17 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
         wsc[n] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr1, soff, rsoff + (n - NW0) * 16 * srowb, 0));
     }
-    const int wsoff = win * C::WIN_BYTES;
+    const int wsoff = win * wwin;
 #pragma unroll
     for (int j = 0; j < C::WLD; ++j) {
 #pragma unroll
       for (int n = 0; n < NW0; ++n)
         wb[S][j][n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, wsoff + 16 * j + n * bstride, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, wsoff + whalf * j + n * bstride, 0));
 #pragma unroll
       for (int n = NW0; n < NB; ++n)
         wb[S][j][n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr1, woff, wsoff + 16 * j + (n - NW0) * bstride, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr1, woff, wsoff + whalf * j + (n - NW0) * bstride, 0));
     }
   };
   auto compute = [&](auto sc) {
@@ -463,7 +474,8 @@ static hipError_t wide_launch(const Shape& s, int T, const uint16_t* act, const 
   const long items = (long)((max_tiles + tg - 1) / tg * tg) * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
   const int grid = (int)((items + kWXcds - 1) / kWXcds * kWXcds);
   hipLaunchKernelGGL((wide_kernel<WT, MODE, MT, NB>), dim3(grid), dim3(kWWaves * kWave), 0, stream, s.H, s.I, s.K,
-                     act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2, tg);
+                     act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2, tg,
+                     s.packed);
   return hipGetLastError();
 }
 

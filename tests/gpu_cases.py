@@ -48,10 +48,21 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def cfg_of(w):
+def cfg_of(w, layout=0):
     import sparse_moe_layer_top_amd as bm
     return bm.Config(w.hidden, w.inter, w.n_experts, w.n_groups, w.topk_groups, w.top_k, w.alpha,
-                     {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight])
+                     {"bf16": bm.W_BF16, "fp8": bm.W_FP8_E4M3, "mxfp4": bm.W_MXFP4}[w.weight], layout)
+
+
+def packed(W):
+    """The expert weights W (row order) in fragment order, through the library's pack entry point; the
+    scales stay as they are."""
+    import sparse_moe_layer_top_amd as bm
+    P = dict(W)
+    for k in ("gate", "up", "down"):
+        P[k] = bm.beam_moe_pack_weights(W[k])
+    torch.cuda.synchronize()
+    return P
 
 
 def guarded(w, seed=0):
@@ -79,12 +90,12 @@ def host_expert_weights(w, seed=0):
     return t, src
 
 
-def run_forward(w, xt, wrt, bt, W):
+def run_forward(w, xt, wrt, bt, W, layout=0):
     import sparse_moe_layer_top_amd as bm
     T = xt.shape[0]
     ids = torch.empty(T, w.top_k, dtype=torch.int32, device=dev())
     wts = torch.empty(T, w.top_k, dtype=torch.float32, device=dev())
-    out = bm.beam_moe_forward(cfg_of(w), xt, wrt, bt, W["gate"], W["up"], W["down"], W.get("s_gate"),
+    out = bm.beam_moe_forward(cfg_of(w, layout), xt, wrt, bt, W["gate"], W["up"], W["down"], W.get("s_gate"),
                               W.get("s_up"), W.get("s_down"), topk_ids_out=ids, topk_w_out=wts)
     torch.cuda.synchronize()
     return out, ids, wts

@@ -10,14 +10,18 @@ from synth import gen
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,block", [("tiny", False), ("tiny", True), ("dense_tiny", False)])
-def test_measure_runs(name, block):
+@pytest.mark.parametrize("name,block,layout", [("tiny", False, 1), ("tiny", True, 1), ("dense_tiny", False, 1),
+                                               ("tiny", False, 0), ("dense_tiny", False, 0)])
+def test_measure_runs(name, block, layout):
     import bench
+    import sparse_moe_layer_top_amd as bm
     w = gen.workload(name)
     dev = torch.device("cuda:0")
     x, wr, b = gen.router_inputs(w, 0)
     W = gen.device_expert_weights(w, 0, dev)
-    m = bench.measure(w, W, x, wr, b, steps=3, warmup=1, block=block)
+    if layout:
+        W = {k: (bm.beam_moe_pack_weights(v) if k in ("gate", "up", "down") else v) for k, v in W.items()}
+    m = bench.measure(w, W, x, wr, b, steps=3, warmup=1, block=block, layout=layout)
     assert m["ms_per_step"] > 0 and m["tokens_per_s"] > 0
     stages = bench.BLOCK_STAGES if block else (bench.DENSE_STAGES if w.n_experts == 1 else bench.STAGES)
     assert set(m["stage_ms"]) == set(stages)
