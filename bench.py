@@ -69,13 +69,14 @@ def kernel_source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, kernel, kind):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this kernel source."""
+def load_traffic(workload, kernel, kind, order):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this kernel source
+    with the weights in this byte order."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash(kind):
+    if d.get("source_hash") != kernel_source_hash(kind) or d.get("weight_order", "rows") != order:
         return None
     return d.get("bytes_per_launch")
 
@@ -142,11 +143,12 @@ def cpu_baseline(w, x_bits, wr, b, seconds_target=20.0, block=False):
                       f"{total_t:.1f} s of oracle time, weight generation excluded"}
 
 
-def gateup_kind(w):
+def gateup_kind(w, packed=True):
     """Which gate/up kernel family the library runs for this workload (mirrors its schedule choice):
     LDS-tiled from 32 rows per expert (the dense path streams up to 1024 tokens); the
     one-workgroup-per-CU kernel for MoE layers at 32..64 rows per expert (any weight type), and from
-    192 rows per expert (bf16) wherever the LDS-tiled one would run, dense included."""
+    192 rows per expert (bf16; 128 with the weights in fragment order) wherever the LDS-tiled one
+    would run, dense included."""
     dense = w.n_experts == 1
     TK, H, I = w.T * w.top_k, w.hidden, w.inter
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
@@ -155,7 +157,7 @@ def gateup_kind(w):
     wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31 and H * I * 2 < 2 ** 31
                and H % (4 * wk) == 0 and I % (4 * wk) == 0)
     wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
-                        or (w.weight == "bf16" and TK >= 192 * w.n_experts and tiled))
+                        or (w.weight == "bf16" and TK >= (128 if packed else 192) * w.n_experts and tiled))
     return "wide" if wide else ("tiled" if tiled else "stream")
 
 
@@ -244,7 +246,7 @@ def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, 
     sec = ms / 1e3
     hbm_gbps = layer_bytes / sec / 1e9
     tflops = layer_flops / sec / 1e12
-    kind = gateup_kind(w)
+    kind = gateup_kind(w, packed=bool(layout))
     res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / sec, 1),
            "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / PEAK_HBM_GBPS, 4),
            "expert_TFLOPs": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -264,7 +266,7 @@ def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, 
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfs / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(w.name, "gateup", kind)
+    roof["traffic"] = load_traffic(w.name, "gateup", kind, "fragments" if layout else "rows")
     roof["kernel"] = KERNEL_NAMES[kind]
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flops_per_launch"] = gu_flops

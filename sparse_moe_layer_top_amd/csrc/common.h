@@ -126,7 +126,8 @@ hipError_t launch_down_tiled(const Shape& s, const uint16_t* h, const void* wd, 
                              int tile_rows, uint16_t* y, hipStream_t stream);
 
 // Expert GEMMs with one workgroup per CU and the weights streamed into registers: which schedule T
-// selects (the balanced one runs gate/up only), its tile rows, launchers.
+// selects (the balanced one runs gate/up, and down too with the weights in fragment order), its tile
+// rows, launchers.
 enum { kWideNone = 0, kWideBalanced = 1, kWideModerate = 2 };
 int wide_schedule(const Shape& s, int T);
 int wide_tile_rows(const Shape& s, int T);

@@ -595,7 +595,7 @@ hipError_t launch_gateup(const Shape& s, int T, const uint16_t* x, const void* w
 hipError_t launch_down(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                        int kparts, float* part, uint16_t* y, hipStream_t stream) {
-  if (wide_schedule(s, T) == kWideModerate)
+  if (wide_schedule(s, T) == kWideModerate || (wide_schedule(s, T) == kWideBalanced && s.packed))
     return launch_down_wide(s, T, h, wd, sd, offsets, tiles, ntiles, max_tiles, y, stream);
   if (use_tiled(s, T))
     return launch_down_tiled(s, h, wd, static_cast<const float*>(sd), offsets, tiles, ntiles, max_tiles,

@@ -1,6 +1,7 @@
 // Grouped expert GEMMs with one workgroup per CU and the weights streamed
-// straight into registers: the prefill gate/up for balanced bf16 layers, and
-// both GEMMs (bf16, fp8 or MXFP4 weights) at a few dozen rows per expert.
+// straight into registers: the prefill gate/up for balanced bf16 layers (and
+// their down GEMM, with the weights in fragment order), and both GEMMs (bf16,
+// fp8 or MXFP4 weights) at a few dozen rows per expert.
 //
 // Same arithmetic as the other expert kernels (each expert a SwiGLU MLP,
 // Reflection Beam 1.0 overview, section "Mixture of Experts"; the SwiGLU
@@ -431,9 +432,13 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 }
 
 // Which one-workgroup-per-CU schedule, if any, a layer takes:
-//   * balanced bf16 (at least 192 rows per expert on average, or a dense layer on the LDS-tiled
-//     path): the gate/up GEMM, 272-row tiles (the LDS-tiled kernel, which skips empty row blocks,
-//     does as well below that); down stays on the LDS-tiled kernel over the same tiles;
+//   * balanced bf16 (at least 192 rows per expert on average, 128 with the weights in fragment
+//     order, or a dense layer on the LDS-tiled path): the gate/up GEMM, 272-row tiles (the
+//     LDS-tiled kernel, which skips empty row blocks, does as well below that: with fragment order,
+//     uniform routing at 96 rows per expert 4.12 against 4.34 ms, at 160 rows 4.88 against 4.81,
+//     the skewed 4096-token batch at 128 rows 5.20 against 5.03); the down GEMM too with the weights
+//     in fragment order (whole-line weight loads: 1.89 against 2.11 ms on the LDS-tiled kernel at
+//     the balanced prefill), else it stays on the LDS-tiled kernel over the same tiles;
 //   * MoE layers with 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row
 //     tiles (a dense layer's single expert would give too few work items).
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
@@ -451,7 +456,7 @@ static int wide_mode(const Shape& s, int T) {
                    s.H % WideCfg<kWtBF16, kWDown, kWModerateMT, 4>::COLS == 0
                ? kWideModerate
                : kWideNone;
-  if (!s.fp8 && !s.mx && tk >= 192L * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
+  if (!s.fp8 && !s.mx && tk >= (s.packed ? 128L : 192L) * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
       use_tiled(s, T))
     return kWideBalanced;
   return kWideNone;
@@ -504,6 +509,9 @@ hipError_t launch_gateup_wide(const Shape& s, int T, const uint16_t* x, const vo
 hipError_t launch_down_wide(const Shape& s, int T, const uint16_t* h, const void* wd, const void* sd,
                             const int32_t* offsets, const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                             uint16_t* y, hipStream_t stream) {
+  if (wide_mode(s, T) == kWideBalanced && s.packed)
+    return wide_launch<kWtBF16, kWDown, kWBalancedMT, 2>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
+                                                         ntiles, max_tiles, y, stream);
   if (wide_mode(s, T) != kWideModerate) return hipErrorInvalidValue;
   if (s.mx)
     return wide_launch<kWtMX, kWDown, kWModerateMT, 4>(s, T, h, wd, nullptr, sd, nullptr, offsets, nullptr, tiles,
