@@ -342,8 +342,9 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true",
                     help="time the steps without the per-stage events (no roofline entry)")
     ap.add_argument("--weight-order", default="fragments", choices=["fragments", "rows"],
-                    help="byte order of the expert weights in HBM: fragment order (written once by "
-                         "beam_moe_pack_weights before timing; the default) or row order")
+                    help="byte order of the expert weights (and MXFP4 scales) in HBM: fragment order "
+                         "(written once by beam_moe_pack_weights / beam_moe_pack_scales before timing; the "
+                         "default) or row order")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -384,6 +385,8 @@ def main():
         import sparse_moe_layer_top_amd as bm
         for k in ("gate", "up", "down"):       # one matrix stack at a time: one extra copy at most
             W[k] = bm.beam_moe_pack_weights(W[k])
+            if w.weight == "mxfp4":
+                W["s_" + k] = bm.beam_moe_pack_scales(W["s_" + k])
             torch.cuda.synchronize()
         log("[bench] expert weights packed into fragment order")
     m = measure(w, W, x_bits, wr, b, steps, warmup, block=args.block, stage_events=not args.no_stage_events,

@@ -65,9 +65,9 @@ typedef enum {
  * streaming GEMMs otherwise. */
 typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1, BEAM_MOE_W_MXFP4 = 2 } beam_moe_wtype;
 
-/* Byte order of the expert weight matrices (the FP8 and MXFP4 scales always stay in row order).
- * The pages fix no storage order; these are two orders of the same bytes, and a forward gives
- * bit-identical results with either.
+/* Byte order of the expert weight matrices and, for MXFP4, of their scale matrices (FP8 scales
+ * always stay in row order).  The pages fix no storage order; these are two orders of the same
+ * bytes, and a forward gives bit-identical results with either.
  *   ROWS       [E, out, in] as described with each entry point: every row's bytes contiguous.
  *   FRAGMENTS  each expert matrix, taken as R rows of B bytes (B = 2*in for bf16, in for e4m3,
  *              in/2 for MXFP4 codes), is cut into blocks of 16 consecutive rows, and each block
@@ -76,7 +76,12 @@ typedef enum { BEAM_MOE_W_BF16 = 0, BEAM_MOE_W_FP8_E4M3 = 1, BEAM_MOE_W_MXFP4 = 
  *              64*f + 16*c + j of the block's row r (r < 16, c < 4, j < 16).  That is the order
  *              in which the 64 lanes of a wavefront take a 16 x 16 x 32 matrix-core operand, so
  *              one 16-byte load per lane reads 1 KB of consecutive addresses.  The matrix keeps
- *              its size; beam_moe_pack_weights writes this order from row order. */
+ *              its size; beam_moe_pack_weights writes this order from row order.
+ *              MXFP4 scale matrices (R rows of S = in/32 bytes) take the same order with 16-byte
+ *              column slices: slice g of block b is 256 bytes at byte 16*S*b + 256*g, whose byte
+ *              16*r + j holds byte 16*g + j of the block's row r (the scales of four 128-deep
+ *              windows of 16 rows, read as two whole cache lines); beam_moe_pack_scales writes
+ *              it.  MXFP4 in this order needs H and I to be multiples of 512. */
 typedef enum { BEAM_MOE_LAYOUT_ROWS = 0, BEAM_MOE_LAYOUT_FRAGMENTS = 1 } beam_moe_wlayout;
 
 typedef enum {
@@ -324,6 +329,14 @@ int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, 
  * rows == 0 is a no-op.  Returns BEAM_MOE_ERR_INVALID for a bad size, a NULL or misaligned
  * pointer, or overlapping buffers.  A byte permutation: exact. */
 int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream);
+
+/* Row order -> fragment order of MXFP4 scale matrices (E8M0 bytes, 16-byte column slices; see
+ * BEAM_MOE_LAYOUT_FRAGMENTS), all E expert matrices of one kind at once.
+ *   rows       R: a multiple of 16 (E*I for s_gate/s_up, E*H for s_down)
+ *   row_bytes  S = in/32: a multiple of 16
+ *   src, dst   as in beam_moe_pack_weights (R*S bytes each, 16-byte aligned, not overlapping)
+ * rows == 0 is a no-op.  Errors as for beam_moe_pack_weights. */
+int beam_moe_pack_scales(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream);
 
 #ifdef __cplusplus
 }

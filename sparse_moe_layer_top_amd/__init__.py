@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     beam_moe_forward,
     beam_moe_forward_noalloc,
     NOALLOC_SCRATCH_BYTES,
+    beam_moe_pack_scales,
     beam_moe_pack_weights,
     beam_moe_permute,
     beam_moe_rms_norm,

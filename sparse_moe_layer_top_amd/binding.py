@@ -111,6 +111,8 @@ def _load():
     lib.beam_mxfp4_quantize.restype = ctypes.c_int
     lib.beam_moe_pack_weights.argtypes = [ctypes.c_int64, I32, P, P, P]
     lib.beam_moe_pack_weights.restype = ctypes.c_int
+    lib.beam_moe_pack_scales.argtypes = [ctypes.c_int64, I32, P, P, P]
+    lib.beam_moe_pack_scales.restype = ctypes.c_int
     return lib
 
 
@@ -416,23 +418,33 @@ def beam_mxfp4_quantize(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
     return codes, scales
 
 
-def beam_moe_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Fragment order of weight matrices w [..., rows, cols] (bf16, or uint8 for e4m3 and MXFP4 codes):
-    the same shape and dtype with the bytes permuted as LAYOUT_FRAGMENTS describes (16-row blocks,
-    1 KB lane-ordered 64-byte column slices).  All leading rows are taken together: a multiple of 16,
-    each row a multiple of 64 bytes."""
+def _pack(fn: str, w: torch.Tensor, slice_bytes: int, dtypes, out: Optional[torch.Tensor]) -> torch.Tensor:
     if w.dim() < 2:
         raise ValueError("w must have at least two dimensions")
-    if w.dtype not in (torch.bfloat16, torch.uint8):
-        raise ValueError(f"w must be bfloat16 or uint8, got {w.dtype}")
+    if w.dtype not in dtypes:
+        raise ValueError(f"w must be one of {dtypes}, got {w.dtype}")
     row_bytes = w.shape[-1] * w.element_size()
     rows = w.numel() // w.shape[-1] if w.shape[-1] else 0
-    if rows % 16 or row_bytes % 64 or row_bytes == 0:
-        raise ValueError(f"rows ({rows}) must be a multiple of 16 and row bytes ({row_bytes}) of 64")
+    if rows % 16 or row_bytes % slice_bytes or row_bytes == 0:
+        raise ValueError(f"rows ({rows}) must be a multiple of 16 and row bytes ({row_bytes}) of {slice_bytes}")
     dev = w.device
     _need(w, "w", w.dtype, tuple(w.shape))
     if out is None:
         out = torch.empty_like(w)
     _need(out, "out", w.dtype, tuple(w.shape), dev)
-    _check("beam_moe_pack_weights", LIB.beam_moe_pack_weights(rows, row_bytes, _ptr(w), _ptr(out), _stream(dev)))
+    _check(fn, getattr(LIB, fn)(rows, row_bytes, _ptr(w), _ptr(out), _stream(dev)))
     return out
+
+
+def beam_moe_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fragment order of weight matrices w [..., rows, cols] (bf16, or uint8 for e4m3 and MXFP4 codes):
+    the same shape and dtype with the bytes permuted as LAYOUT_FRAGMENTS describes (16-row blocks,
+    1 KB lane-ordered 64-byte column slices).  All leading rows are taken together: a multiple of 16,
+    each row a multiple of 64 bytes."""
+    return _pack("beam_moe_pack_weights", w, 64, (torch.bfloat16, torch.uint8), out)
+
+
+def beam_moe_pack_scales(s: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fragment order of MXFP4 scale matrices s [..., rows, cols/32] (uint8 E8M0): 16-row blocks of
+    256-byte slices (16 bytes of each row).  Rows a multiple of 16, each row a multiple of 16 bytes."""
+    return _pack("beam_moe_pack_scales", s, 16, (torch.uint8,), out)

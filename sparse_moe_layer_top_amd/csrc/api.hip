@@ -38,6 +38,9 @@ int check_config(const beam_moe_config* c) {
     return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->weight_type == BEAM_MOE_W_MXFP4 && c->weight_layout == BEAM_MOE_LAYOUT_FRAGMENTS &&
+      (c->hidden % 512 != 0 || c->inter % 512 != 0))
+    return BEAM_MOE_ERR_UNSUPPORTED;   // scale rows in whole 16-byte slices
   if (c->n_experts > beam::kMaxExperts || c->n_groups > 64 || c->top_k > beam::kMaxTopK)
     return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;
@@ -191,6 +194,9 @@ int check_dense_config(const beam_dense_config* c) {
     return BEAM_MOE_ERR_INVALID;
   if (c->hidden % 128 != 0 || c->inter % 128 != 0) return BEAM_MOE_ERR_UNSUPPORTED;
   if (c->weight_type == BEAM_MOE_W_MXFP4 && (c->hidden % 256 != 0 || c->inter % 256 != 0)) return BEAM_MOE_ERR_UNSUPPORTED;
+  if (c->weight_type == BEAM_MOE_W_MXFP4 && c->weight_layout == BEAM_MOE_LAYOUT_FRAGMENTS &&
+      (c->hidden % 512 != 0 || c->inter % 512 != 0))
+    return BEAM_MOE_ERR_UNSUPPORTED;
   return BEAM_MOE_OK;
 }
 
@@ -497,8 +503,13 @@ int beam_mxfp4_quantize(int32_t rows, int32_t cols, const void* w, void* codes, 
   return BEAM_MOE_OK;
 }
 
-int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream) {
-  if (rows < 0 || rows % 16 != 0 || row_bytes <= 0 || row_bytes % 64 != 0) return BEAM_MOE_ERR_INVALID;
+}  // extern "C"
+
+namespace {
+
+// Row order -> fragment order with column slices of slice_bytes (64: weights, 16: MXFP4 scales).
+int pack_fragments(int64_t rows, int32_t row_bytes, int slice_bytes, const void* src, void* dst, void* stream) {
+  if (rows < 0 || rows % 16 != 0 || row_bytes <= 0 || row_bytes % slice_bytes != 0) return BEAM_MOE_ERR_INVALID;
   if (rows > (int64_t)1 << 40 || (int64_t)row_bytes > ((int64_t)1 << 40) / (rows ? rows : 1))
     return BEAM_MOE_ERR_INVALID;
   if (rows == 0) return BEAM_MOE_OK;
@@ -506,8 +517,20 @@ int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
   const uintptr_t n = (uintptr_t)rows * (uintptr_t)row_bytes;
   if (a < b + n && b < a + n) return BEAM_MOE_ERR_INVALID;
-  BEAM_TRY_HIP(beam::launch_pack_weights(rows, row_bytes, src, dst, static_cast<hipStream_t>(stream)));
+  BEAM_TRY_HIP(beam::launch_pack_fragments(rows, row_bytes, slice_bytes, src, dst, static_cast<hipStream_t>(stream)));
   return BEAM_MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_moe_pack_weights(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream) {
+  return pack_fragments(rows, row_bytes, 64, src, dst, stream);
+}
+
+int beam_moe_pack_scales(int64_t rows, int32_t row_bytes, const void* src, void* dst, void* stream) {
+  return pack_fragments(rows, row_bytes, 16, src, dst, stream);
 }
 
 }  // extern "C"

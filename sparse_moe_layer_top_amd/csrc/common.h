@@ -28,7 +28,7 @@ struct Shape {
   int fp8;
   int dense = 0;   // one expert holding every token (a dense SwiGLU MLP): no router, no combine
   int mx = 0;      // MXFP4 weights (E2M1 codes + E8M0 block scales); fp8 is 0 then
-  int packed = 0;  // weight matrices in fragment order (16-row blocks of 1 KB lane-ordered slices)
+  int packed = 0;  // weights (and MXFP4 scales) in fragment order: 16-row blocks of lane-ordered slices
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -100,7 +100,8 @@ hipError_t launch_combine(const Shape& s, int T, const uint16_t* y, const float*
                           const int32_t* pair_to_row, uint16_t* out, hipStream_t stream);
 int down_kparts(const Shape& s, int T);
 int gateup_kparts(const Shape& s, int T);
-hipError_t launch_pack_weights(long rows, int row_bytes, const void* src, void* dst, hipStream_t stream);
+hipError_t launch_pack_fragments(long rows, int row_bytes, int slice_bytes, const void* src, void* dst,
+                                 hipStream_t stream);
 hipError_t launch_mxfp4_quantize(int rows, int cols, const uint16_t* w, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 hipError_t launch_dense_setup(int T, int tile_rows, int32_t* offsets, int32_t* sorted_pairs, int32_t* tiles,

@@ -93,7 +93,10 @@ struct AWin {
 // one 16-byte weight load per weight block (NB blocks of 16 output columns)
 // per step, wst weight elements after the last (row order: the next 64 bytes
 // of the row; fragment order: the block's next 1 KB slice); wrow/arow already
-// include the lane's offset, srow (MXFP4) is the row's scale base.
+// include the lane's offset.  srow (MXFP4) is the row's scale base, t0 the
+// first step's index: step t's four scale bytes sit at 4t in row order, and
+// at 256(t/4) + 4(t%4) in fragment order (srow there already includes the
+// row's 16 bytes within each 256-byte slice of its 16-row block).
 //
 // Weights go straight from HBM into registers in bursts: a window of D steps
 // is issued back to back (each weight row sees D*64 contiguous bytes requested
@@ -107,7 +110,7 @@ struct AWin {
 // the weight ring, which sets how many bytes each CU keeps in flight.
 // sched_barrier fences keep the compiler from reordering the bursts.
 template <int WT, int MT, int NB, int D>
-__device__ __forceinline__ void stream_k(int nsteps, int wst, int wave, int lane,
+__device__ __forceinline__ void stream_k(int nsteps, int wst, int t0, int sfrag, int wave, int lane,
                                          const typename WFrag<WT>::E* const (&wrow)[NB],
                                          const uint8_t* const (&srow)[NB], const uint16_t* const (&arow)[MT],
                                          u32x4 (*lds)[AWin<WT, MT, D>::SLOTS][kWave], f32x4 (&acc)[MT][NB]) {
@@ -140,7 +143,9 @@ __device__ __forceinline__ void stream_k(int nsteps, int wst, int wave, int lane
     if constexpr (W::kBlockScale) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const auto v = *reinterpret_cast<const typename ScaleVec<D>::T*>(srow[nb] + base * 4);
+        const int t = t0 + base;
+        const int so = sfrag ? (t >> 2) * 256 + (t & 3) * 4 : t * 4;
+        const auto v = *reinterpret_cast<const typename ScaleVec<D>::T*>(srow[nb] + so);
         if constexpr (D == 1) {
           sb[buf][nb][0] = v;
         } else {
@@ -275,7 +280,8 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
     const size_t row0 = (size_t)e * I + col0 + (g % G) * 16, row = row0 + l16;   // the block's first row, the lane's
     wr[g] = static_cast<const WE*>(g < G ? wg : wu) +
             (packed ? row0 * HE + lane * (16 / sizeof(WE)) + zs * W::SE * 16 : row * HE + qw + zs * W::SE);
-    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) + row * (H / 32) + zs * (W::SK / 32)
+    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(g < G ? sg : su) +
+                                 (packed ? row0 * (H / 32) + l16 * 16 : row * (H / 32))
                            : nullptr;
   }
   f32x4 acc[MT][2 * G];
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(int H, int I, int K,
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, wave, lane, wr, sr, xr, lds, acc);
+  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, (int)zs, packed, wave, lane, wr, sr, xr, lds, acc);
   if (!active) return;
   if (kparts > 1) {   // raw fp32 sums of this part: gate at part[z][row][col], up at part[z][row][I + col]
 #pragma unroll
@@ -367,14 +373,15 @@ __global__ __launch_bounds__(256) void down_stream_kernel(int H, int I, const ui
     const size_t row0 = (size_t)e * H + c0 + g * 16, row = row0 + l16;
     wr[g] = static_cast<const WE*>(wd) +
             (packed ? row0 * IE + lane * (16 / sizeof(WE)) + zs * W::SE * 16 : row * IE + qw + zs * W::SE);
-    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(sd) + row * (I / 32) + zs * (W::SK / 32) : nullptr;
+    sr[g] = W::kBlockScale ? static_cast<const uint8_t*>(sd) + (packed ? row0 * (I / 32) + l16 * 16 : row * (I / 32))
+                           : nullptr;
   }
   f32x4 acc[MT][2 * G];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, wave, lane, wr, sr, hr, lds, acc);
+  stream_k<WT, MT, 2 * G, D>(nsteps, packed ? 16 * W::SE : W::SE, (int)zs, packed, wave, lane, wr, sr, hr, lds, acc);
   if (!active) return;
 
 #pragma unroll

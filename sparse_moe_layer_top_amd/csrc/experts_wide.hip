@@ -219,7 +219,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword (the lane's block
   // is byte q), a round of the ring's four windows one 16-byte load.  Each row's scale bytes are read
   // once per round, not once per window: with a line's worth of rows per workgroup in flight, lines
-  // fetched for one window do not reliably stay cached until the next.
+  // fetched for one window do not reliably stay cached until the next.  In fragment order a round's
+  // 16 bytes of the 16 rows of a block are one 256-byte slice (row r at 16r), two whole lines.
   const int srowb = KD / 32;
   const size_t smat = (size_t)(MODE == kWGateUp ? I : H) * srowb;
   const __amdgpu_buffer_rsrc_t sr0 =
@@ -231,7 +232,8 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
           ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s1) + e * smat),
                                               (short)0, (int)smat, kRsrcWord3)
           : sr0;
-  const uint32_t soff = (uint32_t)(wc0 + l16) * srowb;
+  const uint32_t soff = packed ? (uint32_t)wc0 * srowb + l16 * 16 : (uint32_t)(wc0 + l16) * srowb;
+  const int sround = packed ? 256 : 16;   // bytes between rounds' scale pieces
 
   // Stage accesses name the stage arrays themselves: the compiler gives each LDS variable its own
   // alias scope, which lets it match a read of a stage to the direct-to-LDS loads into that stage (and
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     __builtin_amdgcn_sched_barrier(0);   // a fixed load order in every issue
     constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
     if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
-      const int rsoff = 16 * (win / kWRing);
+      const int rsoff = sround * (win / kWRing);
 #pragma unroll
       for (int n = 0; n < NW0; ++n)
         wsc[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr0, soff, rsoff + n * 16 * srowb, 0));

@@ -55,12 +55,15 @@ def cfg_of(w, layout=0):
 
 
 def packed(W):
-    """The expert weights W (row order) in fragment order, through the library's pack entry point; the
-    scales stay as they are."""
+    """The expert weights W (row order) in fragment order, through the library's pack entry points:
+    the weight matrices, and MXFP4 scale bytes (uint8); FP8 scales stay as they are."""
     import sparse_moe_layer_top_amd as bm
     P = dict(W)
     for k in ("gate", "up", "down"):
         P[k] = bm.beam_moe_pack_weights(W[k])
+        s = W.get("s_" + k)
+        if s is not None and s.dtype == torch.uint8:
+            P["s_" + k] = bm.beam_moe_pack_scales(s)
     torch.cuda.synchronize()
     return P
 

@@ -20,7 +20,8 @@ def test_measure_runs(name, block, layout):
     x, wr, b = gen.router_inputs(w, 0)
     W = gen.device_expert_weights(w, 0, dev)
     if layout:
-        W = {k: (bm.beam_moe_pack_weights(v) if k in ("gate", "up", "down") else v) for k, v in W.items()}
+        W = {k: (bm.beam_moe_pack_weights(v) if k in ("gate", "up", "down") else
+                 bm.beam_moe_pack_scales(v) if v.dtype == torch.uint8 else v) for k, v in W.items()}
     m = bench.measure(w, W, x, wr, b, steps=3, warmup=1, block=block, layout=layout)
     assert m["ms_per_step"] > 0 and m["tokens_per_s"] > 0
     stages = bench.BLOCK_STAGES if block else (bench.DENSE_STAGES if w.n_experts == 1 else bench.STAGES)

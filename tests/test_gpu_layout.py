@@ -33,6 +33,16 @@ def test_pack_matches_reference(dtype, shape):
     assert np.array_equal(g, F.pack_by_reshape(w))
 
 
+@pytest.mark.parametrize("shape", [(2, 32, 160), (3, 16, 16), (4, 48, 80)])
+def test_pack_scales_matches_reference(shape):
+    import sparse_moe_layer_top_amd as bm
+    rng = np.random.default_rng(6)
+    s = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    got = bm.beam_moe_pack_scales(torch.from_numpy(s).to(C.dev()))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), F.pack_by_reshape(s, 16))
+
+
 def test_pack_real_shape_stack():
     """Four experts of the real gate matrix shape [4, 2560, 5120] bf16: 100 MB."""
     import sparse_moe_layer_top_amd as bm
@@ -92,12 +102,14 @@ def test_forward_same_bytes_in_both_orders(name, T, H, I, E, G, Gk, K, alpha, we
 
 
 @pytest.mark.parametrize("name,T", [("dense_tiny", 7), ("dense_tiny", 64), ("dense_tiny", 1100),
-                                    ("dense_tiny", 2000), ("dense_tiny_mx", 64), ("dense_tiny_mx", 1100),
+                                    ("dense_tiny", 2000), ("dense_mx512", 64), ("dense_mx512", 1100),
                                     ("dense_fp8", 100), ("dense_fp8", 1500)])
 def test_dense_same_bytes_in_both_orders(name, T):
     import sparse_moe_layer_top_amd as bm
     if name == "dense_fp8":
         w = gen.Workload("dense_tiny_fp8", 7, T, 256, 512, 1, 1, 1, 1, 1.0, 0.05, 0.02, "zero", "fp8", 7)
+    elif name == "dense_mx512":     # MXFP4 in fragment order: H and I multiples of 512
+        w = gen.Workload("dense_mx512", 12, T, 512, 512, 1, 1, 1, 1, 1.0, 0.05, 0.02, "zero", "mxfp4", 12)
     else:
         w = gen.workload(name, T)
     C.say(f"[layout dense {name}] T={T} {w.weight}")
