@@ -119,6 +119,25 @@ __device__ __forceinline__ void stage_fill(uint8_t* st, __amdgpu_buffer_rsrc_t r
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (wlds_void*)(st + slot[i]), 16, off[i], soff, 0, 0);
 }
 
+// Row-block counts compiled per tile height: a tile of n row blocks runs the smallest count >= n.
+// 272-row tiles: skewed routing leaves many experts a tile of one or two blocks (the balanced
+// layer's experts take 16 or 17); 96-row tiles: three to six blocks at 64 rows per expert.  (Some
+// larger sets, e.g. with 12 added, make the compiler spill registers in the 272-row down kernel.)
+template <int... Vs>
+struct RowBlockSet {
+  template <typename F>
+  __device__ static void dispatch(int nmb, F&& f) {
+    bool done = false;
+    ((done || nmb > Vs ? void() : (f(std::integral_constant<int, Vs>{}), void(done = true))), ...);
+  }
+};
+template <int MT>
+struct WideRowBlocks;
+template <>
+struct WideRowBlocks<17> : RowBlockSet<1, 2, 4, 8, 16, 17> {};
+template <>
+struct WideRowBlocks<6> : RowBlockSet<2, 3, 4, 5, 6> {};
+
 // (The weight pointers are not restrict: with them the compiler moves each window's weight loads
 // down to their first use, three windows later, which empties the pipeline.)
 template <int WT, int MODE, int MT, int NB>
@@ -130,7 +149,6 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
                                                    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ out,
                                                    long act_bytes, int tgroup, int packed) {
   using C = WideCfg<WT, MODE, MT, NB>;
-  constexpr int GPW = C::GPW;
   constexpr bool FP8 = WT == kWtFP8, MX = WT == kWtMX;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
@@ -164,273 +182,281 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const int l16 = lane % 16, q = lane / 16;
 
-  // Activation load groups of this wave: g = wave + 8i, rows 8g + lane/8 (clamped to the tile), as
-  // byte offsets into a buffer resource over the activation rows (gate/up: all of x, below 2^31
-  // bytes, checked by the launcher; down: the tile's own rows of h).  Loads of groups past the last
-  // or wholly past the tile's rows go past the buffer's end, into the spare slot.
-  const uint16_t* abase = MODE == kWGateUp ? act : act + (size_t)(lo + r0) * KD;
-  const uint32_t abytes = MODE == kWGateUp ? (uint32_t)act_bytes : (uint32_t)rows * KD * 2;
-  const __amdgpu_buffer_rsrc_t arsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(abase), (short)0, (int)abytes, kRsrcWord3);
-  uint32_t aoff[GPW];
-  int aslot[GPW];
-#pragma unroll
-  for (int i = 0; i < GPW; ++i) {
-    const int gw = wave + kWWaves * i;
-    const bool live = gw < C::GROUPS && 8 * gw < rows;
-    const int g = gw < C::GROUPS ? gw : C::GROUPS;
-    aslot[i] = g * 1024;
-    const int r = min(8 * g + lane / 8, rows - 1);
-    const uint32_t row = MODE == kWGateUp ? (uint32_t)(sorted_pairs[lo + r0 + r] / K) : (uint32_t)r;
-    aoff[i] = live ? (row * (uint32_t)KD + ((lane % 8) ^ (lane / 8) ^ (g % 2)) * 8) * 2 : kPastEnd;
-  }
-  // This wave's weight rows through buffer resources over the expert's matrices: gate/up, rows
-  // c, c + 16, ... of both matrices (c the wave's first intermediate column); down, NB consecutive
-  // blocks of 16 rows.  Block n is 16n rows past the first (soffset).
-  const int rowb = KD / C::WIN_K * C::WIN_BYTES;                          // bytes per weight row
-  const size_t wmat = (size_t)(MODE == kWGateUp ? I : H) * rowb;          // bytes per expert matrix
-  const __amdgpu_buffer_rsrc_t wr0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(static_cast<const uint8_t*>(w0) + e * wmat), (short)0, (int)wmat, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr1 =
-      MODE == kWGateUp ? __builtin_amdgcn_make_buffer_rsrc(
-                             const_cast<uint8_t*>(static_cast<const uint8_t*>(w1) + e * wmat), (short)0, (int)wmat,
-                             kRsrcWord3)
-                       : wr0;
-  constexpr int WCOLS = MODE == kWGateUp ? 8 * NB : 16 * NB;   // this wave's output columns
-  const int wc0 = jn * C::COLS + wave * WCOLS;
-  // The lane's 16 bytes of a window.  Row order: row wc0 + l16, bf16 bytes [32q + 16a, +16) of the window
-  // (half a), fp8 and MXFP4 bytes [16q, +16).  Fragment order (a window is one 1 KB slice per 64 bytes of
-  // row, chunk c of row r at 16(r + 16c)): bf16 slice q/2, chunk 2(q%2) + a; fp8, MXFP4 chunk q.
-  const uint32_t woff = packed ? (uint32_t)wc0 * rowb + (WT == kWtBF16 ? (q / 2) * 1024 + (q % 2) * 512 + l16 * 16
-                                                                       : lane * 16)
-                               : (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
-  const int wwin = packed ? 16 * C::WIN_BYTES : C::WIN_BYTES;   // bytes between windows
-  const int whalf = packed ? 256 : 16;                          // bytes between a bf16 window's two loads
-  const int bstride = 16 * rowb;         // bytes between blocks of 16 weight rows
-  // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB groups)
-  // (MXFP4: chunk 4(q%2) + t of the lane's half q/2, t = 0..3)
-  constexpr int NSL = MX ? 4 : 2;   // MFMA slices per window
-  int roff[NSL];
-#pragma unroll
-  for (int t = 0; t < NSL; ++t) {
-    const int c = MX ? 4 * (q % 2) + t : 2 * q + t;
-    roff[t] = (MX ? (q / 2) * C::SUB : 0) + (l16 / 8) * 1024 + ((l16 % 8) * 8 + (c ^ (l16 % 8) ^ (l16 / 8))) * 16;
-  }
-  // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword (the lane's block
-  // is byte q), a round of the ring's four windows one 16-byte load.  Each row's scale bytes are read
-  // once per round, not once per window: with a line's worth of rows per workgroup in flight, lines
-  // fetched for one window do not reliably stay cached until the next.  In fragment order a round's
-  // 16 bytes of the 16 rows of a block are one 256-byte slice (row r at 16r), two whole lines.
-  const int srowb = KD / 32;
-  const size_t smat = (size_t)(MODE == kWGateUp ? I : H) * srowb;
-  const __amdgpu_buffer_rsrc_t sr0 =
-      MX ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s0) + e * smat),
-                                             (short)0, (int)smat, kRsrcWord3)
-         : wr0;
-  const __amdgpu_buffer_rsrc_t sr1 =
-      MX && MODE == kWGateUp
-          ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s1) + e * smat),
-                                              (short)0, (int)smat, kRsrcWord3)
-          : sr0;
-  const uint32_t soff = packed ? (uint32_t)wc0 * srowb + l16 * 16 : (uint32_t)(wc0 + l16) * srowb;
-  const int sround = packed ? 256 : 16;   // bytes between rounds' scale pieces
-
-  // Stage accesses name the stage arrays themselves: the compiler gives each LDS variable its own
-  // alias scope, which lets it match a read of a stage to the direct-to-LDS loads into that stage (and
-  // not to loads into the others) when it places its waits.
-  // one word of each of this wave's slots in a stage: the compiler waits for all of the wave's loads into it
-  auto stage_probe = [&](const uint8_t* st) -> uint32_t {
-    uint32_t v = 0;
-#pragma unroll
-    for (int h = 0; h < C::HALVES; ++h)
-#pragma unroll
-      for (int i = 0; i < GPW; ++i) v |= *reinterpret_cast<const uint32_t*>(st + h * C::SUB + aslot[i] + lane * 16);
-    return v;
-  };
-
-  u32x4 wb[kWRing][C::WLD][NB];   // [slot][16-byte load][block]; gate/up blocks: NB/2 gate then NB/2 up
-  u32x4 wsc[MX ? NB : 1];    // MXFP4 scale dwords of a round's four windows (loaded with ring slot 0)
-  u32x4 wsck[MX ? NB : 1];   // the same, kept through the round while the next round's are in flight
-  f32x4 acc[MT][NB];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nwin = KD / C::WIN_K;   // a multiple of kWRing (checked by the launcher)
-  // Window win into ring slot S.  Past the end the last window is issued again (into a slot nothing
-  // reads): every round issues the same loads.
-  auto issue = [&](auto sc, int win) {
-    constexpr int S = decltype(sc)::value;
-#pragma unroll
-    for (int h = 0; h < C::HALVES; ++h)
-      stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
-    __builtin_amdgcn_sched_barrier(0);   // a fixed load order in every issue
-    constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
-    if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
-      const int rsoff = sround * (win / kWRing);
-#pragma unroll
-      for (int n = 0; n < NW0; ++n)
-        wsc[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr0, soff, rsoff + n * 16 * srowb, 0));
-#pragma unroll
-      for (int n = NW0; n < NB; ++n)
-        wsc[n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr1, soff, rsoff + (n - NW0) * 16 * srowb, 0));
+  // The tile's row blocks pick one of a few compiled row-block counts MTE <= MT: the loop then runs
+  // the MFMAs, activation loads and LDS reads of those blocks only (the LDS layout stays MT's).
+  auto body = [&](auto mte) {
+    constexpr int MTE = decltype(mte)::value;
+    constexpr int GROUPS_E = 2 * MTE;                        // 8-row activation load groups per window
+    constexpr int GPW = (GROUPS_E + kWWaves - 1) / kWWaves;
+    // Activation load groups of this wave: g = wave + 8i, rows 8g + lane/8 (clamped to the tile), as
+    // byte offsets into a buffer resource over the activation rows (gate/up: all of x, below 2^31
+    // bytes, checked by the launcher; down: the tile's own rows of h).  Loads of groups past the last
+    // or wholly past the tile's rows go past the buffer's end, into the spare slot.
+    const uint16_t* abase = MODE == kWGateUp ? act : act + (size_t)(lo + r0) * KD;
+    const uint32_t abytes = MODE == kWGateUp ? (uint32_t)act_bytes : (uint32_t)rows * KD * 2;
+    const __amdgpu_buffer_rsrc_t arsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(abase), (short)0, (int)abytes, kRsrcWord3);
+    uint32_t aoff[GPW];
+    int aslot[GPW];
+  #pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int gw = wave + kWWaves * i;
+      const bool live = gw < GROUPS_E && 8 * gw < rows;
+      const int g = gw < GROUPS_E ? gw : GROUPS_E;
+      aslot[i] = g * 1024;
+      const int r = min(8 * g + lane / 8, rows - 1);
+      const uint32_t row = MODE == kWGateUp ? (uint32_t)(sorted_pairs[lo + r0 + r] / K) : (uint32_t)r;
+      aoff[i] = live ? (row * (uint32_t)KD + ((lane % 8) ^ (lane / 8) ^ (g % 2)) * 8) * 2 : kPastEnd;
     }
-    const int wsoff = win * wwin;
-#pragma unroll
-    for (int j = 0; j < C::WLD; ++j) {
-#pragma unroll
-      for (int n = 0; n < NW0; ++n)
-        wb[S][j][n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, wsoff + whalf * j + n * bstride, 0));
-#pragma unroll
-      for (int n = NW0; n < NB; ++n)
-        wb[S][j][n] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr1, woff, wsoff + whalf * j + (n - NW0) * bstride, 0));
+    // This wave's weight rows through buffer resources over the expert's matrices: gate/up, rows
+    // c, c + 16, ... of both matrices (c the wave's first intermediate column); down, NB consecutive
+    // blocks of 16 rows.  Block n is 16n rows past the first (soffset).
+    const int rowb = KD / C::WIN_K * C::WIN_BYTES;                          // bytes per weight row
+    const size_t wmat = (size_t)(MODE == kWGateUp ? I : H) * rowb;          // bytes per expert matrix
+    const __amdgpu_buffer_rsrc_t wr0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(w0) + e * wmat), (short)0, (int)wmat, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wr1 =
+        MODE == kWGateUp ? __builtin_amdgcn_make_buffer_rsrc(
+                               const_cast<uint8_t*>(static_cast<const uint8_t*>(w1) + e * wmat), (short)0, (int)wmat,
+                               kRsrcWord3)
+                         : wr0;
+    constexpr int WCOLS = MODE == kWGateUp ? 8 * NB : 16 * NB;   // this wave's output columns
+    const int wc0 = jn * C::COLS + wave * WCOLS;
+    // The lane's 16 bytes of a window.  Row order: row wc0 + l16, bf16 bytes [32q + 16a, +16) of the window
+    // (half a), fp8 and MXFP4 bytes [16q, +16).  Fragment order (a window is one 1 KB slice per 64 bytes of
+    // row, chunk c of row r at 16(r + 16c)): bf16 slice q/2, chunk 2(q%2) + a; fp8, MXFP4 chunk q.
+    const uint32_t woff = packed ? (uint32_t)wc0 * rowb + (WT == kWtBF16 ? (q / 2) * 1024 + (q % 2) * 512 + l16 * 16
+                                                                         : lane * 16)
+                                 : (uint32_t)(wc0 + l16) * rowb + q * (C::WIN_BYTES / 4);
+    const int wwin = packed ? 16 * C::WIN_BYTES : C::WIN_BYTES;   // bytes between windows
+    const int whalf = packed ? 256 : 16;                          // bytes between a bf16 window's two loads
+    const int bstride = 16 * rowb;         // bytes between blocks of 16 weight rows
+    // where lane (r, q) finds chunk 2q + a of row r of a 16-row block (two 1 KB groups)
+    // (MXFP4: chunk 4(q%2) + t of the lane's half q/2, t = 0..3)
+    constexpr int NSL = MX ? 4 : 2;   // MFMA slices per window
+    int roff[NSL];
+  #pragma unroll
+    for (int t = 0; t < NSL; ++t) {
+      const int c = MX ? 4 * (q % 2) + t : 2 * q + t;
+      roff[t] = (MX ? (q / 2) * C::SUB : 0) + (l16 / 8) * 1024 + ((l16 % 8) * 8 + (c ^ (l16 % 8) ^ (l16 / 8))) * 16;
     }
-  };
-  auto compute = [&](auto sc) {
-    constexpr int S = decltype(sc)::value;
-    const uint8_t* st = stage(sc);
-    float msc[MX ? NB : 1];
-    if constexpr (MX) {
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        if constexpr (S == 0) wsck[n] = wsc[n];   // the next issue into slot 0 reloads wsc
-        msc[n] = e8m0_to_f32((wsck[n][S] >> (8 * q)) & 0xFFu);
+    // MXFP4 scales: KD/32 bytes per weight row; a window's four blocks are one dword (the lane's block
+    // is byte q), a round of the ring's four windows one 16-byte load.  Each row's scale bytes are read
+    // once per round, not once per window: with a line's worth of rows per workgroup in flight, lines
+    // fetched for one window do not reliably stay cached until the next.  In fragment order a round's
+    // 16 bytes of the 16 rows of a block are one 256-byte slice (row r at 16r), two whole lines.
+    const int srowb = KD / 32;
+    const size_t smat = (size_t)(MODE == kWGateUp ? I : H) * srowb;
+    const __amdgpu_buffer_rsrc_t sr0 =
+        MX ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s0) + e * smat),
+                                               (short)0, (int)smat, kRsrcWord3)
+           : wr0;
+    const __amdgpu_buffer_rsrc_t sr1 =
+        MX && MODE == kWGateUp
+            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(s1) + e * smat),
+                                                (short)0, (int)smat, kRsrcWord3)
+            : sr0;
+    const uint32_t soff = packed ? (uint32_t)wc0 * srowb + l16 * 16 : (uint32_t)(wc0 + l16) * srowb;
+    const int sround = packed ? 256 : 16;   // bytes between rounds' scale pieces
+
+    // Stage accesses name the stage arrays themselves: the compiler gives each LDS variable its own
+    // alias scope, which lets it match a read of a stage to the direct-to-LDS loads into that stage (and
+    // not to loads into the others) when it places its waits.
+    // one word of each of this wave's slots in a stage: the compiler waits for all of the wave's loads into it
+    auto stage_probe = [&](const uint8_t* st) -> uint32_t {
+      uint32_t v = 0;
+  #pragma unroll
+      for (int h = 0; h < C::HALVES; ++h)
+  #pragma unroll
+        for (int i = 0; i < GPW; ++i) v |= *reinterpret_cast<const uint32_t*>(st + h * C::SUB + aslot[i] + lane * 16);
+      return v;
+    };
+
+    u32x4 wb[kWRing][C::WLD][NB];   // [slot][16-byte load][block]; gate/up blocks: NB/2 gate then NB/2 up
+    u32x4 wsc[MX ? NB : 1];    // MXFP4 scale dwords of a round's four windows (loaded with ring slot 0)
+    u32x4 wsck[MX ? NB : 1];   // the same, kept through the round while the next round's are in flight
+    f32x4 acc[MTE][NB];
+  #pragma unroll
+    for (int m = 0; m < MTE; ++m)
+  #pragma unroll
+      for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nwin = KD / C::WIN_K;   // a multiple of kWRing (checked by the launcher)
+    // Window win into ring slot S.  Past the end the last window is issued again (into a slot nothing
+    // reads): every round issues the same loads.
+    auto issue = [&](auto sc, int win) {
+      constexpr int S = decltype(sc)::value;
+  #pragma unroll
+      for (int h = 0; h < C::HALVES; ++h)
+        stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
+      __builtin_amdgcn_sched_barrier(0);   // a fixed load order in every issue
+      constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
+      if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
+        const int rsoff = sround * (win / kWRing);
+  #pragma unroll
+        for (int n = 0; n < NW0; ++n)
+          wsc[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr0, soff, rsoff + n * 16 * srowb, 0));
+  #pragma unroll
+        for (int n = NW0; n < NB; ++n)
+          wsc[n] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr1, soff, rsoff + (n - NW0) * 16 * srowb, 0));
       }
-    }
-#pragma unroll
-    for (int a = 0; a < NSL; ++a) {
-      bf16x8 b[NB];
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        if constexpr (MX) {
-          b[n] = e2m1x8_to_bf16x8(wb[S][0][n][a], msc[n]);
-        } else if constexpr (FP8) {
-          const u32x4 v = wb[S][0][n];
-          b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{v[0], v[1]} : u32x2{v[2], v[3]});
-        } else {
-          b[n] = __builtin_bit_cast(bf16x8, wb[S][a][n]);
+      const int wsoff = win * wwin;
+  #pragma unroll
+      for (int j = 0; j < C::WLD; ++j) {
+  #pragma unroll
+        for (int n = 0; n < NW0; ++n)
+          wb[S][j][n] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr0, woff, wsoff + whalf * j + n * bstride, 0));
+  #pragma unroll
+        for (int n = NW0; n < NB; ++n)
+          wb[S][j][n] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr1, woff, wsoff + whalf * j + (n - NW0) * bstride, 0));
+      }
+    };
+    auto compute = [&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      const uint8_t* st = stage(sc);
+      float msc[MX ? NB : 1];
+      if constexpr (MX) {
+  #pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          if constexpr (S == 0) wsck[n] = wsc[n];   // the next issue into slot 0 reloads wsc
+          msc[n] = e8m0_to_f32((wsck[n][S] >> (8 * q)) & 0xFFu);
         }
       }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + m * 2048 + roff[a]);
-#pragma unroll
-        for (int n = 0; n < NB; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
+  #pragma unroll
+      for (int a = 0; a < NSL; ++a) {
+        bf16x8 b[NB];
+  #pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          if constexpr (MX) {
+            b[n] = e2m1x8_to_bf16x8(wb[S][0][n][a], msc[n]);
+          } else if constexpr (FP8) {
+            const u32x4 v = wb[S][0][n];
+            b[n] = e4m3x8_to_bf16x8(a == 0 ? u32x2{v[0], v[1]} : u32x2{v[2], v[3]});
+          } else {
+            b[n] = __builtin_bit_cast(bf16x8, wb[S][a][n]);
+          }
+        }
+  #pragma unroll
+        for (int m = 0; m < MTE; ++m) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(st + m * 2048 + roff[a]);
+  #pragma unroll
+          for (int n = 0; n < NB; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
+        }
       }
+      constexpr int kAhead = MTE < 3 ? MTE : 3;
+      constexpr int kReads = NSL * MTE;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
+  #pragma unroll
+      for (int i = 0; i < kReads - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);     // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NB * kAhead, 0);
+    };
+    // Open window w (ring slot S): this wave's loads into stage S have landed (reading back a word of
+    // each slot makes the compiler wait for them), then the barrier: every wave's have, and every wave
+    // is done with window w-1, whose stage and registers the next issue reuses.
+    auto open = [&](auto sc, int w) {
+      constexpr int S = decltype(sc)::value;
+      const uint32_t probe = stage_probe(stage(sc));
+      asm volatile("" ::"v"(probe) : "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(std::integral_constant<int, (S + kWAhead) % kWRing>{}, min(w + kWAhead, nwin - 1));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto run = [&](auto sc) {
+      compute(sc);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Each round enters with windows w .. w+2 in flight, issued in the same order on both paths into
+    // the loop (prologue and back edge), so the compiler's view of the pending loads at the loop's head
+    // is exact and its waits stay precise.
+    issue(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(std::integral_constant<int, 2>{}, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int w = 0; w < nwin; w += kWRing) {
+      open(std::integral_constant<int, 0>{}, w);
+      run(std::integral_constant<int, 0>{});
+      open(std::integral_constant<int, 1>{}, w + 1);
+      run(std::integral_constant<int, 1>{});
+      open(std::integral_constant<int, 2>{}, w + 2);
+      run(std::integral_constant<int, 2>{});
+      open(std::integral_constant<int, 3>{}, w + 3);
+      run(std::integral_constant<int, 3>{});
     }
-    constexpr int kAhead = MT < 3 ? MT : 3;
-    constexpr int kReads = NSL * MT;
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
-#pragma unroll
-    for (int i = 0; i < kReads - kAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);     // MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+
+    // Epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block.  Stage the bf16 output
+    // tile row-major in LDS, rows [OUT_ROWS*j, +OUT_ROWS) in stage j (after the repeated tail loads
+    // into stages 0..2 have landed and every wave is past the last window), then store whole rows.
+    {
+      uint32_t probe = 0;
+      probe |= stage_probe(lds0);
+      probe |= stage_probe(lds1);
+      probe |= stage_probe(lds2);
+      asm volatile("" ::"v"(probe) : "memory");
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NB * kAhead, 0);
-  };
-  // Open window w (ring slot S): this wave's loads into stage S have landed (reading back a word of
-  // each slot makes the compiler wait for them), then the barrier: every wave's have, and every wave
-  // is done with window w-1, whose stage and registers the next issue reuses.
-  auto open = [&](auto sc, int w) {
-    constexpr int S = decltype(sc)::value;
-    const uint32_t probe = stage_probe(stage(sc));
-    asm volatile("" ::"v"(probe) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(std::integral_constant<int, (S + kWAhead) % kWRing>{}, min(w + kWAhead, nwin - 1));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto run = [&](auto sc) {
-    compute(sc);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Each round enters with windows w .. w+2 in flight, issued in the same order on both paths into
-  // the loop (prologue and back edge), so the compiler's view of the pending loads at the loop's head
-  // is exact and its waits stay precise.
-  issue(std::integral_constant<int, 0>{}, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(std::integral_constant<int, 1>{}, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(std::integral_constant<int, 2>{}, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int w = 0; w < nwin; w += kWRing) {
-    open(std::integral_constant<int, 0>{}, w);
-    run(std::integral_constant<int, 0>{});
-    open(std::integral_constant<int, 1>{}, w + 1);
-    run(std::integral_constant<int, 1>{});
-    open(std::integral_constant<int, 2>{}, w + 2);
-    run(std::integral_constant<int, 2>{});
-    open(std::integral_constant<int, 3>{}, w + 3);
-    run(std::integral_constant<int, 3>{});
-  }
-
-  // Epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block.  Stage the bf16 output
-  // tile row-major in LDS, rows [OUT_ROWS*j, +OUT_ROWS) in stage j (after the repeated tail loads
-  // into stages 0..2 have landed and every wave is past the last window), then store whole rows.
-  {
-    uint32_t probe = 0;
-    probe |= stage_probe(lds0);
-    probe |= stage_probe(lds1);
-    probe |= stage_probe(lds2);
-    asm volatile("" ::"v"(probe) : "memory");
-  }
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  auto orow = [&](int r) -> uint8_t* {
-    const int j = r / C::OUT_ROWS, rr = r % C::OUT_ROWS;
-    uint8_t* b = j == 0 ? lds0 : j == 1 ? lds1 : j == 2 ? lds2 : lds3;
-    return b + rr * C::CST;
-  };
-  const int nmb = (rows + 15) / 16;
-  if constexpr (MODE == kWGateUp) {
-#pragma unroll
-    for (int n = 0; n < NB / 2; ++n) {
-      const int c = wave * WCOLS + n * 16 + l16;   // column within the tile
-      const float sg = FP8 ? static_cast<const float*>(s0)[(size_t)e * I + jn * C::COLS + c] : 1.f;
-      const float su = FP8 ? static_cast<const float*>(s1)[(size_t)e * I + jn * C::COLS + c] : 1.f;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < nmb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + q * 4 + i;
-            const float g = acc[m][n][i] * sg, u = acc[m][n + NB / 2][i] * su;
-            *reinterpret_cast<uint16_t*>(orow(r) + c * 2) = f32_to_bf16(silu(g) * u);
+    auto orow = [&](int r) -> uint8_t* {
+      const int j = r / C::OUT_ROWS, rr = r % C::OUT_ROWS;
+      uint8_t* b = j == 0 ? lds0 : j == 1 ? lds1 : j == 2 ? lds2 : lds3;
+      return b + rr * C::CST;
+    };
+    const int nmb = (rows + 15) / 16;
+    if constexpr (MODE == kWGateUp) {
+  #pragma unroll
+      for (int n = 0; n < NB / 2; ++n) {
+        const int c = wave * WCOLS + n * 16 + l16;   // column within the tile
+        const float sg = FP8 ? static_cast<const float*>(s0)[(size_t)e * I + jn * C::COLS + c] : 1.f;
+        const float su = FP8 ? static_cast<const float*>(s1)[(size_t)e * I + jn * C::COLS + c] : 1.f;
+  #pragma unroll
+        for (int m = 0; m < MTE; ++m) {
+          if (m < nmb) {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = m * 16 + q * 4 + i;
+              const float g = acc[m][n][i] * sg, u = acc[m][n + NB / 2][i] * su;
+              *reinterpret_cast<uint16_t*>(orow(r) + c * 2) = f32_to_bf16(silu(g) * u);
+            }
+          }
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int c = wave * WCOLS + n * 16 + l16;
+        const float sd = FP8 ? static_cast<const float*>(s0)[(size_t)e * H + jn * C::COLS + c] : 1.f;
+  #pragma unroll
+        for (int m = 0; m < MTE; ++m) {
+          if (m < nmb) {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = m * 16 + q * 4 + i;
+              *reinterpret_cast<uint16_t*>(orow(r) + c * 2) = f32_to_bf16(acc[m][n][i] * sd);
+            }
           }
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int c = wave * WCOLS + n * 16 + l16;
-      const float sd = FP8 ? static_cast<const float*>(s0)[(size_t)e * H + jn * C::COLS + c] : 1.f;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < nmb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = m * 16 + q * 4 + i;
-            *reinterpret_cast<uint16_t*>(orow(r) + c * 2) = f32_to_bf16(acc[m][n][i] * sd);
-          }
-        }
-      }
+    __syncthreads();
+    constexpr int CPR = C::COLS / 8;   // 16-byte chunks per output row
+    const int ldo = MODE == kWGateUp ? I : H;
+    uint16_t* const obase = out + (size_t)(lo + r0) * ldo + (size_t)jn * C::COLS;
+    for (int idx = threadIdx.x; idx < rows * CPR; idx += kWWaves * kWave) {
+      const int r = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<u32x4*>(obase + (size_t)r * ldo + ch * 8) = *reinterpret_cast<const u32x4*>(orow(r) + ch * 16);
     }
-  }
-  __syncthreads();
-  constexpr int CPR = C::COLS / 8;   // 16-byte chunks per output row
-  const int ldo = MODE == kWGateUp ? I : H;
-  uint16_t* const obase = out + (size_t)(lo + r0) * ldo + (size_t)jn * C::COLS;
-  for (int idx = threadIdx.x; idx < rows * CPR; idx += kWWaves * kWave) {
-    const int r = idx / CPR, ch = idx % CPR;
-    *reinterpret_cast<u32x4*>(obase + (size_t)r * ldo + ch * 8) = *reinterpret_cast<const u32x4*>(orow(r) + ch * 16);
-  }
+  };
+  WideRowBlocks<MT>::dispatch((rows + 15) / 16, body);
 }
 
 // Which one-workgroup-per-CU schedule, if any, a layer takes:
