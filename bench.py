@@ -147,8 +147,8 @@ def gateup_kind(w, packed=True):
     """Which gate/up kernel family the library runs for this workload (mirrors its schedule choice):
     LDS-tiled from 32 rows per expert (the dense path streams up to 1024 tokens); the
     one-workgroup-per-CU kernel for MoE layers at 32..64 rows per expert (any weight type), and from
-    192 rows per expert (bf16; 128 with the weights in fragment order) wherever the LDS-tiled one
-    would run, dense included."""
+    192 rows per expert (bf16; above 64 with the weights in fragment order) wherever the LDS-tiled
+    one would run, dense included."""
     dense = w.n_experts == 1
     TK, H, I = w.T * w.top_k, w.hidden, w.inter
     tiled = (TK / w.n_experts >= 32 and H % 256 == 0 and I % 128 == 0 and not (dense and w.T <= 1024)
@@ -157,7 +157,7 @@ def gateup_kind(w, packed=True):
     wide_ok = (TK >= 32 * w.n_experts and w.T * H * 2 < 2 ** 31 and H * I * 2 < 2 ** 31
                and H % (4 * wk) == 0 and I % (4 * wk) == 0)
     wide = wide_ok and ((not dense and TK <= 64 * w.n_experts and H % 512 == 0 and I % 256 == 0)
-                        or (w.weight == "bf16" and TK >= (128 if packed else 192) * w.n_experts and tiled))
+                        or (w.weight == "bf16" and TK >= (64 if packed else 192) * w.n_experts and tiled))
     return "wide" if wide else ("tiled" if tiled else "stream")
 
 

@@ -460,13 +460,13 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
 }
 
 // Which one-workgroup-per-CU schedule, if any, a layer takes:
-//   * balanced bf16 (at least 192 rows per expert on average, 128 with the weights in fragment
-//     order, or a dense layer on the LDS-tiled path): the gate/up GEMM, 272-row tiles (the
-//     LDS-tiled kernel, which skips empty row blocks, does as well below that: with fragment order,
-//     uniform routing at 96 rows per expert 4.12 against 4.34 ms, at 160 rows 4.88 against 4.81,
-//     the skewed 4096-token batch at 128 rows 5.20 against 5.03); the down GEMM too with the weights
-//     in fragment order (whole-line weight loads: 1.89 against 2.11 ms on the LDS-tiled kernel at
-//     the balanced prefill), else it stays on the LDS-tiled kernel over the same tiles;
+//   * balanced bf16 (more than 64 rows per expert on average with the weights in fragment order,
+//     at least 192 in row order, or a dense layer on the LDS-tiled path): the gate/up GEMM, 272-row
+//     tiles, each running only the row blocks it holds (with fragment order, against the LDS-tiled
+//     kernel: uniform routing at 66, 100 and 134 rows per expert 3.74 / 3.82 / 3.96 against
+//     3.86 / 3.97 / 4.29 ms, skewed routing at 94 rows 4.04 against 4.54); the down GEMM too with
+//     the weights in fragment order (whole-line weight loads: 1.89 against 2.11 ms on the LDS-tiled
+//     kernel at the balanced prefill), else it stays on the LDS-tiled kernel over the same tiles;
 //   * MoE layers with 32 to 64 rows per expert on average (bf16, fp8 or MXFP4): both GEMMs, 96-row
 //     tiles (a dense layer's single expert would give too few work items).
 // The reductions must be whole rounds of the window ring, the column blocks must divide I and H,
@@ -484,7 +484,7 @@ static int wide_mode(const Shape& s, int T) {
                    s.H % WideCfg<kWtBF16, kWDown, kWModerateMT, 4>::COLS == 0
                ? kWideModerate
                : kWideNone;
-  if (!s.fp8 && !s.mx && tk >= (s.packed ? 128L : 192L) * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
+  if (!s.fp8 && !s.mx && tk >= (s.packed ? 64L : 192L) * s.E && s.I % WideCfg<kWtBF16, kWGateUp, kWBalancedMT, 2>::COLS == 0 &&
       use_tiled(s, T))
     return kWideBalanced;
   return kWideNone;
