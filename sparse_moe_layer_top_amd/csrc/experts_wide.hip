@@ -61,11 +61,12 @@
 //     contiguous ranges, so the workgroups of one expert share its
 //     activation rows in one L2.
 //
-// Balanced bf16 gate/up (272-row tiles, NB = 2): the loads set the time.  A
-// window brings 34 KB of activation rows (L2 hits) per 32 KB of weights (HBM)
-// through each CU's vector memory path, whose address unit is then about 71%
-// busy; the MFMAs run about 53% of the kernel's cycles and are mostly hidden
-// behind the loads (timing variants without MFMAs are 6% faster).
+// Balanced bf16 GEMMs (272-row tiles, NB = 2).  A window brings 34 KB of
+// activation rows (L2 hits) per 32 KB of weights (HBM) through each CU's
+// vector memory path.  With row-order weights its address unit was about 71%
+// busy and set the time (MFMAs 53% of the cycles); with fragment-order weights
+// it is about 55% busy, the MFMAs about 60%, and the chip holds its power
+// limit at about 1.7 GHz.
 // At 96-row tiles (NB = 4) the work is HBM-bound: a window brings 12 KB of
 // activations and 64 KB (bf16) of weights per CU.
 #include <type_traits>

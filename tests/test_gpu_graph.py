@@ -15,9 +15,9 @@ from tests import gpu_cases as C
 pytestmark = pytest.mark.gpu
 
 
-def _capture_and_replay(w, W, seeds, src=None):
+def _capture_and_replay(w, W, seeds, src=None, layout=0):
     import sparse_moe_layer_top_amd as bm
-    cfg = C.cfg_of(w)
+    cfg = C.cfg_of(w, layout)
     d = C.dev()
     inputs = [C.guarded(w, s) for s in seeds]
     xt = C.to_bf16(inputs[0][1])
@@ -35,7 +35,7 @@ def _capture_and_replay(w, W, seeds, src=None):
     # direct results for every input set, with separate buffers
     direct = []
     for spec, x, wr, b in inputs:
-        o, i, ww = C.run_forward(w, *C.router_tensors(x, wr, b), W)
+        o, i, ww = C.run_forward(w, *C.router_tensors(x, wr, b), W, layout)
         direct.append((C.bits_of(o), i.cpu().numpy(), ww.cpu().numpy()))
 
     side = torch.cuda.Stream()
@@ -66,7 +66,7 @@ def _capture_and_replay(w, W, seeds, src=None):
         assert np.array_equal(ids.cpu().numpy(), i)
         assert np.array_equal(wts.cpu().numpy().view(np.uint32), ww.view(np.uint32))
         # eager work between replays: a direct call on the other input set
-        C.run_forward(w, *C.router_tensors(*inputs[(k + 1) % len(inputs)][1:]), W)
+        C.run_forward(w, *C.router_tensors(*inputs[(k + 1) % len(inputs)][1:]), W, layout)
     return inputs, direct
 
 
@@ -182,3 +182,17 @@ def test_graph_tiny_dense(T):
         bm.beam_dense_mlp_forward(cfg, x, W["gate"], W["up"], W["down"], out=out, workspace=ws)
 
     _replay_against_direct(run, set_inputs, [out], 2, f"tiny dense T={T}")
+
+
+@pytest.mark.parametrize("name,T,H,I,weight", [("tiny", 64, 256, 128, "bf16"), ("wide272", 1500, 256, 256, "bf16"),
+                                               ("moderate_mx", 230, 512, 512, "mxfp4")])
+def test_graph_fragment_order(name, T, H, I, weight):
+    """Weights (and MXFP4 scales) in fragment order, on the streaming, 272-row and 96-row MXFP4 schedules:
+    every replay gives the direct call's bytes, and those are the row-order forward's bytes."""
+    w = gen.Workload("graph_frag_" + name, 1, T, H, I, 32, 8, 4, 8, 2.5, 0.05, 0.02, "zero", weight, 1)
+    W, _ = C.host_expert_weights(w, 4)
+    P = C.packed(W)
+    inputs, direct = _capture_and_replay(w, P, seeds=[4, 5], layout=1)
+    for (spec, x, wr, b), (o, i, ww) in zip(inputs, direct):
+        o_rows, _, _ = C.run_forward(w, *C.router_tensors(x, wr, b), W, 0)
+        assert np.array_equal(C.bits_of(o_rows), o)
