@@ -103,7 +103,7 @@ typedef struct {
   int32_t top_k;        /* K: 1..8, K <= Gk * E / G */
   float routed_scale;   /* alpha: finite */
   int32_t weight_type;  /* beam_moe_wtype */
-  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down */
+  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down (and of MXFP4 s_gate, s_up, s_down) */
 } beam_moe_config;
 
 /* Largest T accepted by every entry point. */
@@ -277,7 +277,7 @@ typedef struct {
   int32_t hidden;       /* H: multiple of 128 (256 for MXFP4) */
   int32_t inter;        /* I: multiple of 128 (256 for MXFP4) */
   int32_t weight_type;  /* beam_moe_wtype */
-  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down */
+  int32_t weight_layout;  /* beam_moe_wlayout of w_gate, w_up and w_down (and of MXFP4 s_gate, s_up, s_down) */
 } beam_dense_config;
 
 /* Workspace bytes of beam_dense_mlp_forward for T tokens (host only, pure): the
