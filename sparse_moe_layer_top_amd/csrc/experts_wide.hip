@@ -166,15 +166,31 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
   const int KD = MODE == kWGateUp ? H : I;                  // reduction length
   const int NT = (MODE == kWGateUp ? I : H) / C::COLS;      // column blocks per tile
   // Work items in groups of tgroup row tiles, column block outer and tile inner within a group (the
-  // last group padded; tgroup = 1: one tile's column blocks after another).
-  const int nitems = (ntiles[0] + tgroup - 1) / tgroup * tgroup * NT;
+  // last group padded; tgroup = 1: one tile's column blocks after another).  tgroup = 0: the row
+  // tiles of one expert form the group (the tile list holds an expert's tiles in a row, tile k of
+  // the expert at rows k * ROWS), so an expert with several tiles streams each weight column block
+  // for all of them at once, and one-tile experts keep the tile order.
+  const int nitems = tgroup == 0 ? ntiles[0] * NT : (ntiles[0] + tgroup - 1) / tgroup * tgroup * NT;
   const int per_xcd = (nitems + kWXcds - 1) / kWXcds;
   const int slot = blockIdx.x / kWXcds;
   if (slot >= per_xcd) return;
   const int item = (blockIdx.x % kWXcds) * per_xcd + slot;
   if (item >= nitems) return;
-  const int grp = item / (tgroup * NT), rr = item % (tgroup * NT);
-  const int tile = grp * tgroup + rr % tgroup, jn = rr / tgroup;
+  int tile, jn;
+  if (tgroup == 0) {
+    // the expert's items span the same range as in tile order: the tile there names the expert
+    const int tp = item / NT;
+    const int ep = tiles[2 * tp];
+    const int tfirst = tp - tiles[2 * tp + 1] / C::ROWS;                       // the expert's first tile
+    const int ne = (offsets[ep + 1] - offsets[ep] + C::ROWS - 1) / C::ROWS;     // and its tile count
+    const int local = item - NT * tfirst;
+    jn = local / ne;
+    tile = tfirst + local % ne;
+  } else {
+    const int grp = item / (tgroup * NT), rr = item % (tgroup * NT);
+    tile = grp * tgroup + rr % tgroup;
+    jn = rr / tgroup;
+  }
   if (tile >= ntiles[0]) return;
   const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
   const int lo = offsets[e];
@@ -503,9 +519,12 @@ static hipError_t wide_launch(const Shape& s, int T, const uint16_t* act, const 
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles, uint16_t* out,
                               hipStream_t stream) {
   using C = WideCfg<WT, MODE, MT, NB>;
-  // a dense layer's row tiles all use the same weights: groups of them run each column block together
-  const int tg = s.dense ? kWDenseTileGroup : 1;
-  const long items = (long)((max_tiles + tg - 1) / tg * tg) * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
+  // a dense layer's row tiles all use the same weights: groups of them run each column block together;
+  // at 272-row tiles an expert's own tiles do (skewed routing: 4.55 -> 4.35 ms; one-tile experts
+  // unchanged)
+  const int tg = s.dense ? kWDenseTileGroup : (MT == kWBalancedMT ? 0 : 1);
+  const int tgr = tg ? tg : 1;
+  const long items = (long)((max_tiles + tgr - 1) / tgr * tgr) * ((MODE == kWGateUp ? s.I : s.H) / C::COLS);
   const int grid = (int)((items + kWXcds - 1) / kWXcds * kWXcds);
   hipLaunchKernelGGL((wide_kernel<WT, MODE, MT, NB>), dim3(grid), dim3(kWWaves * kWave), 0, stream, s.H, s.I, s.K,
                      act, w0, w1, s0, s1, offsets, sorted_pairs, tiles, ntiles, out, (long)T * s.H * 2, tg,
