@@ -49,13 +49,15 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int E, int nchunks, int3
   int run = 0;
   if (e < E) {
     int c = 0;
-    for (; c + 4 <= nchunks; c += 4) {
-      const int v0 = counts[(size_t)(c + 0) * E + e], v1 = counts[(size_t)(c + 1) * E + e];
-      const int v2 = counts[(size_t)(c + 2) * E + e], v3 = counts[(size_t)(c + 3) * E + e];
-      counts[(size_t)(c + 0) * E + e] = run; run += v0;
-      counts[(size_t)(c + 1) * E + e] = run; run += v1;
-      counts[(size_t)(c + 2) * E + e] = run; run += v2;
-      counts[(size_t)(c + 3) * E + e] = run; run += v3;
+    for (; c + 16 <= nchunks; c += 16) {   // 16 loads in flight, then the running sum in chunk order
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = counts[(size_t)(c + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        counts[(size_t)(c + j) * E + e] = run;
+        run += v[j];
+      }
     }
     for (; c < nchunks; ++c) {
       const int v = counts[(size_t)c * E + e];
@@ -63,19 +65,43 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int E, int nchunks, int3
       run += v;
     }
   }
-  tot[e] = (e < E) ? run : 0;
-  ntl[e] = (e < E && tile_rows > 0) ? (run + tile_rows - 1) / tile_rows : 0;
-  __syncthreads();
-  if (e == 0) {   // E <= 256 sequential adds: negligible next to the chunk loop
-    int acc = 0, tacc = 0;
-    for (int i = 0; i < E; ++i) {
-      const int v = tot[i], n = ntl[i];
-      tot[i] = acc; acc += v;
-      ntl[i] = tacc; tacc += n;
+  // exclusive prefix sums over the experts of the row counts and the tile counts: within each wave by
+  // shuffles, then across the four waves through LDS (integer sums: any order gives the same result)
+  const int mytot = (e < E) ? run : 0;
+  const int myntl = (e < E && tile_rows > 0) ? (run + tile_rows - 1) / tile_rows : 0;
+  const int lane = e % kWave, wv = e / kWave;
+  int it = mytot, in = myntl;   // inclusive within the wave
+#pragma unroll
+  for (int d = 1; d < kWave; d *= 2) {
+    const int ot = __shfl_up(it, d), on = __shfl_up(in, d);
+    if (lane >= d) {
+      it += ot;
+      in += on;
     }
-    offsets[E] = acc;
-    if (tile_rows > 0) ntiles[0] = tacc;
   }
+  if (lane == kWave - 1) {
+    tot[wv] = it;
+    ntl[wv] = in;
+  }
+  __syncthreads();
+  int bt = 0, bn = 0;   // the sums of the waves before this one
+  for (int j = 0; j < wv; ++j) {
+    bt += tot[j];
+    bn += ntl[j];
+  }
+  const int nw = (int)blockDim.x / kWave;
+  if (e == 0) {
+    int at = 0, an = 0;
+    for (int j = 0; j < nw; ++j) {
+      at += tot[j];
+      an += ntl[j];
+    }
+    offsets[E] = at;
+    if (tile_rows > 0) ntiles[0] = an;
+  }
+  __syncthreads();
+  tot[e] = bt + it - mytot;
+  ntl[e] = bn + in - myntl;
   __syncthreads();
   if (e < E) {
     offsets[e] = tot[e];
