@@ -12,8 +12,9 @@
 //                  MFMA: W_router (fp32) is split exactly into three bf16
 //                  planes, w = hi + mid + lo, so every product x*w-part is
 //                  exact (x is bf16) and the sums accumulate in fp32;
-//   router_select: one workgroup per token: sum the partials in a fixed order,
-//                  add the bias, sigmoid, then the selection in one wave.
+//   router_select: sum the partials in a fixed order, add the bias, sigmoid,
+//                  then the selection in one wave (a workgroup per token at
+//                  small T, a wave per token at large T).
 #include "common.h"
 
 namespace beam {
@@ -136,7 +137,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// One workgroup per token: thread e sums expert e's K-split partials in a
+// Small T (deep K-splits): one workgroup per token: thread e sums expert e's K-split partials in a
 // fixed order (coalesced across threads), adds the bias and takes the sigmoid;
 // wave 0 then runs the group-limited selection on the scores in LDS.
 __global__ __launch_bounds__(256) void router_select_kernel(int T, int E, int G, int Gk, int K, int ks,
@@ -241,6 +242,143 @@ __global__ __launch_bounds__(256) void router_select_kernel(int T, int E, int G,
   }
 }
 
+// Large T: one wave per token, four tokens per workgroup.  Lane l sums the K-split
+// partials of experts l, l + 64, ... in a fixed order (coalesced across the
+// lanes), adds the bias and takes the sigmoid; the wave then runs the
+// group-limited selection on its token's scores in LDS.  The phases pass data
+// through the wave's own LDS rows, ordered by wave-level fences.
+constexpr int kSelTok = 4;          // tokens (waves) per workgroup
+constexpr int kSelWaveMinT = 4096;  // from this many tokens the wave-per-token form runs
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(kSelTok * kWave) void router_select_wave_kernel(
+    int T, int E, int G, int Gk, int K, int ks, float alpha, const float* __restrict__ partial,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wout) {
+  __shared__ float s_sc_all[kSelTok][kMaxExperts];
+  __shared__ float s_gs_all[kSelTok][64];
+  __shared__ int s_keep_all[kSelTok][64];
+  __shared__ float s_sel_all[kSelTok][kMaxTopK];
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kSelTok + wv;
+  if (t >= T) return;   // a whole wave; no workgroup barrier follows
+  float* s_sc = s_sc_all[wv];
+  float* s_gs = s_gs_all[wv];
+  int* s_keep = s_keep_all[wv];
+  float* s_sel = s_sel_all[wv];
+  const size_t stride = (size_t)T * E;
+  constexpr int kEL = kMaxExperts / kWave;   // experts per lane: lane, lane + 64, ...
+  const float* p = partial + (size_t)t * E + lane;
+  float z[kEL];
+#pragma unroll
+  for (int j = 0; j < kEL; ++j) z[j] = 0.f;
+  int q = 0;
+  for (; q + 8 <= ks; q += 8) {   // every expert's loads issued ahead of the adds, which stay in part order
+    float v[kEL][8];
+#pragma unroll
+    for (int j = 0; j < kEL; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = lane + kWave * j < E ? p[(q + i) * stride + kWave * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kEL; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[j] += v[j][i];
+  }
+  for (; q < ks; ++q) {
+    float v[kEL];
+#pragma unroll
+    for (int j = 0; j < kEL; ++j) v[j] = lane + kWave * j < E ? p[q * stride + kWave * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kEL; ++j) z[j] += v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kEL; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E) {
+      float zz = z[j];
+      if (bias) zz += bias[e];
+      s_sc[e] = 1.0f / (1.0f + expf(-zz));
+    }
+  }
+  wave_lds_sync();
+  const int gsz = E / G;
+  // group score = top1 + top2 of the group's scores
+  if (lane < G) {
+    float a1 = -1.f, a2 = -1.f;
+    for (int i = 0; i < gsz; ++i) {
+      const float v = s_sc[lane * gsz + i];
+      if (v > a1) { a2 = a1; a1 = v; } else if (v > a2) { a2 = v; }
+    }
+    s_gs[lane] = a1 + a2;
+  }
+  wave_lds_sync();
+  // keep the Gk best groups (ties: lower group index)
+  if (lane < G) {
+    const float mine = s_gs[lane];
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+      const float o = s_gs[g];
+      rank += (o > mine) || (o == mine && g < lane);
+    }
+    s_keep[lane] = rank < Gk;
+  }
+  wave_lds_sync();
+  {
+    // lane owns experts 4*lane .. 4*lane+3
+    float sc[4];
+    bool cand[4], sel[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      const bool ok = e < E;
+      sc[j] = ok ? s_sc[e] : -1.f;
+      cand[j] = ok && s_keep[e / gsz];
+      sel[j] = false;
+    }
+    // K rounds of a wave-wide argmax over the remaining candidates (ties: lower id)
+    for (int r = 0; r < K; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (cand[j] && !sel[j]) {
+          const uint64_t key = (static_cast<uint64_t>(__float_as_uint(sc[j])) << 32) |
+                               (0xFFFFFFFFu - static_cast<uint32_t>(lane * 4 + j));
+          best = key > best ? key : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const uint32_t win = 0xFFFFFFFFu - static_cast<uint32_t>(best);
+      if ((win >> 2) == static_cast<uint32_t>(lane)) sel[win & 3] = true;
+    }
+    // slot of each chosen expert = number of chosen experts with a lower id
+    uint64_t m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = __ballot(sel[j]);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int pos = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pos += __popcll(m[j] & below);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sel[j]) {
+        s_sel[pos] = sc[j];
+        ids[(size_t)t * K + pos] = lane * 4 + j;
+        ++pos;
+      }
+    }
+  }
+  wave_lds_sync();
+  if (lane < K) {
+    float den = 0.f;
+    for (int k = 0; k < K; ++k) den += s_sel[k];   // sequential, ascending expert id
+    wout[(size_t)t * K + lane] = (s_sel[lane] / den) * alpha;
+  }
+}
+
 hipError_t launch_router_logits(const Shape& s, int T, int ks, const uint16_t* x, const float* wr,
                                 float* partial, hipStream_t stream) {
   dim3 grid((T + kRTok - 1) / kRTok, (s.E + kRExp - 1) / kRExp, ks);
@@ -250,9 +388,16 @@ hipError_t launch_router_logits(const Shape& s, int T, int ks, const uint16_t* x
 
 hipError_t launch_router_select(const Shape& s, int T, int ks, const float* partial, const float* b,
                                 int32_t* ids, float* w, hipStream_t stream) {
-  dim3 grid(T);
-  hipLaunchKernelGGL(router_select_kernel, grid, dim3(256), 0, stream, T, s.E, s.G, s.Gk, s.K, ks, s.alpha,
-                     partial, b, ids, w);
+  // Both forms add the same partials in the same order.  At small T the K-split is deep (40 parts at 64
+  // tokens) and a thread per expert keeps each chain short (decode: 12.7 against 19 us); at large T one
+  // wave per token needs a quarter of the waves (8192 tokens: 31 against 48 us).
+  if (T >= kSelWaveMinT) {
+    hipLaunchKernelGGL(router_select_wave_kernel, dim3((T + kSelTok - 1) / kSelTok), dim3(kSelTok * kWave), 0,
+                       stream, T, s.E, s.G, s.Gk, s.K, ks, s.alpha, partial, b, ids, w);
+  } else {
+    hipLaunchKernelGGL(router_select_kernel, dim3(T), dim3(256), 0, stream, T, s.E, s.G, s.Gk, s.K, ks, s.alpha,
+                       partial, b, ids, w);
+  }
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ def test_tiny_forward_full(seed):
     C.check_out(C.bits_of(out), ref["out"])
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 63, 64, 65, 130, 257, 1000])
+@pytest.mark.parametrize("T", [1, 2, 7, 63, 64, 65, 130, 257, 1000, 4095, 4097])
 def test_tiny_ragged_tokens(T):
     w = gen.workload("tiny", T)
     spec, x, wr, b = C.guarded(w, 5)
