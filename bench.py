@@ -22,7 +22,9 @@ The metric has two halves: HBM GB/s at decode and MFMA TFLOP/s at prefill.
 The default run (the decode workload, T = 64) therefore also measures the
 balanced prefill workload (T = 8192) on the same expert weights and puts it
 in the same line as "prefill" (ms, tokens/s, MFMA TFLOP/s and fraction,
-stage rooflines, its own CPU-oracle sample); --no-prefill leaves it out.
+stage rooflines, its own CPU-oracle sample, and for scale the vendor GEMM
+library's sustained bf16 rate on large square products on the same GPU);
+--no-prefill leaves it out.
 --steps / --warmup set the headline workload's counts; the prefill part
 uses its own defaults.
 """
@@ -326,6 +328,37 @@ def describe(w, block=False):
             + (f"; whole sublayer: RMSNorm before and after, residual mix at step {BLOCK_STEP}" if block else ""))
 
 
+GEMM_CEILING_SHAPES = [(8192, 8192, 8192), (16384, 16384, 16384), (8192, 5120, 40960)]
+
+
+def gemm_ceiling(torch, dev, shapes=GEMM_CEILING_SHAPES, reps=20, warmup=5):
+    """Dense bf16 rate of the vendor GEMM library on large products [M, K] x [K, N] (plain 2-D matmul of
+    contiguous operands), timed with events on the current stream: the rate the chip sustains on
+    MFMA-bound work, for scale against the datasheet peak."""
+    out = {"gemm_ceiling": [], "peak_TFLOPs": PEAK_BF16_TFLOPS}
+    for (M, K, N) in shapes:
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+        b = torch.randn(K, N, device=dev, generator=g).to(torch.bfloat16)
+        c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        for _ in range(warmup):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+        out["gemm_ceiling"].append({"M": M, "K": K, "N": N, "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                                    "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"[bench] matmul {M}x{K}x{N}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
+        del a, b, c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +381,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run 5 plain device copies of MIB MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="instead of the layer, time the vendor GEMM library (torch.matmul, bf16, contiguous "
+                         "operands) on large products (two square, one the dense prefill gate/up shape): the dense "
+                         "bf16 rate this GPU sustains, for scale against the 2.5 PFLOP/s datasheet peak")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
@@ -370,6 +407,9 @@ def main():
             c.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.gemm_ceiling:
+        print(json.dumps(gemm_ceiling(torch, dev)), flush=True)
         return
     w = gen.workload(args.workload)
     if w.n_experts == 1 and args.block:
@@ -417,6 +457,14 @@ def main():
         pref = {"workload": describe(wp), "T": wp.T, "bias": wp.bias, "steps": psteps, "warmup": pwarm,
                 "target": {"ms_per_step": 4.10, "mfma_frac": 0.5}}
         pref.update(pm)
+        # for scale: the vendor library's sustained rate on large square products on this same GPU
+        ceil = gemm_ceiling(torch, dev, shapes=GEMM_CEILING_SHAPES[:2])
+        best = max(g["TFLOPs"] for g in ceil["gemm_ceiling"])
+        ceil["best_TFLOPs"] = best
+        ceil["layer_expert_TFLOPs_over_best"] = round(pm["expert_TFLOPs"] / best, 4)
+        gu = pm.get("stages", {}).get("gateup", {}).get("TFLOPs")
+        ceil["gateup_TFLOPs_over_best"] = round(gu / best, 4) if gu else None
+        pref["vendor_gemm_ceiling"] = ceil
         if not args.no_cpu_baseline:
             log("[bench] CPU oracle baseline (prefill)")
             pref["cpu_baseline"] = cpu_baseline(wp, px, pwr, pb)

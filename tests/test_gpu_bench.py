@@ -30,3 +30,13 @@ def test_measure_runs(name, block, layout):
     assert m["roofline"]["kernel"] and m["roofline"]["frac"] > 0
     if w.n_experts > 1:
         assert m["routing"]["touched_experts"] > 0
+
+
+def test_gemm_ceiling_reports_each_shape():
+    import bench
+    dev = torch.device("cuda:0")
+    r = bench.gemm_ceiling(torch, dev, shapes=[(256, 512, 384)], reps=2, warmup=1)
+    (g,) = r["gemm_ceiling"]
+    assert (g["M"], g["K"], g["N"]) == (256, 512, 384)
+    assert g["ms"] > 0 and g["TFLOPs"] > 0
+    assert abs(g["frac"] - g["TFLOPs"] / bench.PEAK_BF16_TFLOPS) < 1e-3
