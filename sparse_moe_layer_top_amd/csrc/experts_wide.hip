@@ -70,6 +70,7 @@
 // At 96-row tiles (NB = 4) the work is HBM-bound: a window brings 12 KB of
 // activations and 64 KB (bf16) of weights per CU.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -118,6 +119,19 @@ __device__ __forceinline__ void stage_fill(uint8_t* st, __amdgpu_buffer_rsrc_t r
 #pragma unroll
   for (int i = 0; i < n; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (wlds_void*)(st + slot[i]), 16, off[i], soff, 0, 0);
+}
+
+// Scheduling groups of one window's compute: NI times (NB MFMAs, one DS read, and the i-th share of NV
+// vector memory loads, spread evenly).
+template <int N>
+__device__ __forceinline__ void vmem_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(0x010, N, 0);
+}
+template <int NB, int NV, int NI, int... Is>
+__device__ __forceinline__ void mfma_read_load_groups(std::integer_sequence<int, Is...>) {
+  ((__builtin_amdgcn_sched_group_barrier(0x008, NB, 0), __builtin_amdgcn_sched_group_barrier(0x100, 1, 0),
+    vmem_group<(Is + 1) * NV / NI - Is * NV / NI>()),
+   ...);
 }
 
 // Row-block counts compiled per tile height: a tile of n row blocks runs the smallest count >= n.
@@ -301,12 +315,14 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     const int nwin = KD / C::WIN_K;   // a multiple of kWRing (checked by the launcher)
     // Window win into ring slot S.  Past the end the last window is issued again (into a slot nothing
     // reads): every round issues the same loads.
-    auto issue = [&](auto sc, int win) {
+    // (fenced: the direct-to-LDS loads are kept ahead of the weight loads by a scheduling barrier, as the
+    // prologue needs; the loop's issues instead leave the placement to compute's scheduling groups)
+    auto issue = [&](auto sc, int win, auto fenced) {
       constexpr int S = decltype(sc)::value;
   #pragma unroll
       for (int h = 0; h < C::HALVES; ++h)
         stage_fill(stage(sc) + h * C::SUB, arsrc, aslot, aoff, GPW, (win * C::HALVES + h) * kWWin * 2);
-      __builtin_amdgcn_sched_barrier(0);   // a fixed load order in every issue
+      if constexpr (decltype(fenced)::value) __builtin_amdgcn_sched_barrier(0);   // a fixed load order
       constexpr int NW0 = MODE == kWGateUp ? NB / 2 : NB;   // blocks from the first matrix
       if constexpr (MX && S == 0) {   // window win is a round's first (or, past the end, the last window)
         const int rsoff = sround * (win / kWRing);
@@ -363,30 +379,32 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
           for (int n = 0; n < NB; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[n], acc[m][n], 0, 0, 0);
         }
       }
+      // The next issue's loads (NV of them, issued in this region) go evenly between the MFMA groups: issued
+      // all at once after the barrier, a window's loads from the eight waves queue at the CU's address
+      // unit, and a wave waiting to issue its last load cannot start its MFMAs.
       constexpr int kAhead = MTE < 3 ? MTE : 3;
       constexpr int kReads = NSL * MTE;
+      constexpr int NI = kReads - kAhead;
+      constexpr int NV = GPW * C::HALVES + C::WLD * NB + (MX && S == (kWRing - kWAhead) % kWRing ? NB : 0);
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // DS reads
-  #pragma unroll
-      for (int i = 0; i < kReads - kAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);     // MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      mfma_read_load_groups<NB, NV, NI>(std::make_integer_sequence<int, NI>{});
       __builtin_amdgcn_sched_group_barrier(0x008, NB * kAhead, 0);
     };
     // Open window w (ring slot S): this wave's loads into stage S have landed (reading back a word of
     // each slot makes the compiler wait for them), then the barrier: every wave's have, and every wave
     // is done with window w-1, whose stage and registers the next issue reuses.
     auto open = [&](auto sc, int w) {
-      constexpr int S = decltype(sc)::value;
       const uint32_t probe = stage_probe(stage(sc));
       asm volatile("" ::"v"(probe) : "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue(std::integral_constant<int, (S + kWAhead) % kWRing>{}, min(w + kWAhead, nwin - 1));
-      asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto run = [&](auto sc) {
+    // Window w's MFMAs, with window w+3's loads issued among them (into the stage and registers every
+    // wave was done with at the barrier).
+    auto run = [&](auto sc, int w) {
+      constexpr int S = decltype(sc)::value;
+      issue(std::integral_constant<int, (S + kWAhead) % kWRing>{}, min(w + kWAhead, nwin - 1), std::false_type{});
       compute(sc);
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -394,21 +412,21 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     // Each round enters with windows w .. w+2 in flight, issued in the same order on both paths into
     // the loop (prologue and back edge), so the compiler's view of the pending loads at the loop's head
     // is exact and its waits stay precise.
-    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 0>{}, 0, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 1>{}, 1, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
-    issue(std::integral_constant<int, 2>{}, 2);
+    issue(std::integral_constant<int, 2>{}, 2, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     for (int w = 0; w < nwin; w += kWRing) {
       open(std::integral_constant<int, 0>{}, w);
-      run(std::integral_constant<int, 0>{});
+      run(std::integral_constant<int, 0>{}, w);
       open(std::integral_constant<int, 1>{}, w + 1);
-      run(std::integral_constant<int, 1>{});
+      run(std::integral_constant<int, 1>{}, w + 1);
       open(std::integral_constant<int, 2>{}, w + 2);
-      run(std::integral_constant<int, 2>{});
+      run(std::integral_constant<int, 2>{}, w + 2);
       open(std::integral_constant<int, 3>{}, w + 3);
-      run(std::integral_constant<int, 3>{});
+      run(std::integral_constant<int, 3>{}, w + 3);
     }
 
     // Epilogue: C[r][c] sits in lane (c = l%16, r = 4q + i) of each 16x16 block.  Stage the bf16 output
