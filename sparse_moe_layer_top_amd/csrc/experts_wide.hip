@@ -55,6 +55,10 @@
 //     it filled in that stage (the compiler waits for those loads), and the
 //     barrier then publishes the stage to every wave; it also says every wave
 //     is done with the stage (and the registers) the next issue reuses.
+//   * That issue (window w+3's loads) goes between the MFMAs of window w,
+//     evenly, not in one block after the barrier: there the eight waves'
+//     loads queued at the CU's address unit at once, and a wave could start
+//     its MFMAs only once its last load had been accepted.
 //   * The output tile is staged through LDS and stored as whole 16-byte
 //     chunks along rows.
 //   * Work items (row tile, column block) are dealt to the 8 XCDs in
@@ -390,10 +394,10 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
       mfma_read_load_groups<NB, NV, NI>(std::make_integer_sequence<int, NI>{});
       __builtin_amdgcn_sched_group_barrier(0x008, NB * kAhead, 0);
     };
-    // Open window w (ring slot S): this wave's loads into stage S have landed (reading back a word of
+    // Open the window in ring slot S: this wave's loads into stage S have landed (reading back a word of
     // each slot makes the compiler wait for them), then the barrier: every wave's have, and every wave
-    // is done with window w-1, whose stage and registers the next issue reuses.
-    auto open = [&](auto sc, int w) {
+    // is done with the window before, whose stage and registers the next issue reuses.
+    auto open = [&](auto sc) {
       const uint32_t probe = stage_probe(stage(sc));
       asm volatile("" ::"v"(probe) : "memory");
       __builtin_amdgcn_s_barrier();
@@ -419,13 +423,13 @@ __global__ __launch_bounds__(512) void wide_kernel(int H, int I, int K, const ui
     issue(std::integral_constant<int, 2>{}, 2, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     for (int w = 0; w < nwin; w += kWRing) {
-      open(std::integral_constant<int, 0>{}, w);
+      open(std::integral_constant<int, 0>{});
       run(std::integral_constant<int, 0>{}, w);
-      open(std::integral_constant<int, 1>{}, w + 1);
+      open(std::integral_constant<int, 1>{});
       run(std::integral_constant<int, 1>{}, w + 1);
-      open(std::integral_constant<int, 2>{}, w + 2);
+      open(std::integral_constant<int, 2>{});
       run(std::integral_constant<int, 2>{}, w + 2);
-      open(std::integral_constant<int, 3>{}, w + 3);
+      open(std::integral_constant<int, 3>{});
       run(std::integral_constant<int, 3>{}, w + 3);
     }
 
