@@ -258,6 +258,10 @@ def measure(w, W, x_bits, wr, b, steps, warmup, block=False, stage_events=True, 
                                           "mean_load": TK / w.n_experts, "zero_load_experts": int((load == 0).sum())}}
     if not stage_events:
         return res
+    # each step's own span (its first stage event to its last): spread over the timed steps
+    per_step = np.array([evs[i][0].elapsed_time(evs[i][nev - 1]) for i in range(steps)])
+    res["step_ms"] = {"median": round(float(np.median(per_step)), 4), "min": round(float(per_step.min()), 4),
+                      "max": round(float(per_step.max()), 4)}
     t_gu = stage_ms["gateup"] / 1e3
     # the dominant kernel's roofline: the resource whose floor (work / peak) is the larger one binds
     gbps = gu_bytes / t_gu / 1e9

@@ -27,6 +27,8 @@ def test_measure_runs(name, block, layout):
     stages = bench.BLOCK_STAGES if block else (bench.DENSE_STAGES if w.n_experts == 1 else bench.STAGES)
     assert set(m["stage_ms"]) == set(stages)
     assert all(np.isfinite(v) and v >= 0 for v in m["stage_ms"].values())
+    st = m["step_ms"]
+    assert 0 < st["min"] <= st["median"] <= st["max"]
     assert m["roofline"]["kernel"] and m["roofline"]["frac"] > 0
     if w.n_experts > 1:
         assert m["routing"]["touched_experts"] > 0
