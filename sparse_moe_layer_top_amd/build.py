@@ -3,12 +3,15 @@
     python sparse_moe_layer_top_amd/build.py
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into sparse_moe_layer_top_amd/libbeam_moe.so.
+then linked into sparse_moe_layer_top_amd/libbeam_moe.so.  The compiler's
+per-kernel resource report is checked on the way: a kernel that spills
+registers or uses scratch memory fails the build.
 """
 from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -33,12 +36,43 @@ FLAGS = [
 ]
 
 
+# the compiler's per-kernel resource report (registers, scratch, spills), checked after each compile
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"SGPRs Spill|VGPRs Spill): (\S+)")
+
+
+def kernel_resources(remarks: str) -> list:
+    """One dict per kernel from the compiler's resource remarks: name, VGPRs, AGPRs, scratch bytes per
+    lane, occupancy, SGPR and VGPR spills."""
+    out = []
+    for line in remarks.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            out.append({"kernel": val})
+        elif out:
+            out[-1][key.split(" [")[0]] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
+def spilling(kernels: list) -> list:
+    """Kernels that use scratch memory or spill registers (each such access is a round trip to memory)."""
+    return [k for k in kernels
+            if k.get("ScratchSize", 0) != 0 or k.get("VGPRs Spill", 0) != 0 or k.get("SGPRs Spill", 0) != 0]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    bad = spilling(kernel_resources(r.stderr))
+    if bad:
+        raise RuntimeError(f"kernels in {src} spill registers or use scratch memory: {bad}")
     return obj
 
 
